@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs for one GPU's expert-parallel share of an MoE FFN.
+
+This module is shared by the CPU oracle and the HIP path. It holds no step of
+the method's arithmetic: no routing, no layout, no FFN and no combine. It only
+draws seeded random numbers and packs them into the byte formats that both
+sides receive (bf16 bit patterns; e4m3 bytes plus fp32 block scales).
+
+Workload shapes follow the X-Stage paper's MegaMoE evaluation (section 5.1,
+expert parallelism over eight ranks: eight source slices stand in for the
+eight ranks) with model shapes chosen to match DeepSeek-V3 and Qwen3-MoE
+expert FFNs, since the paper's own model table (Table 2) names shapes without
+giving their dimensions.
+
+Draw order per workload (numpy ``default_rng`` over one ``SeedSequence`` per
+workload, one child stream per tensor and per expert, so any single expert's
+weights can be regenerated on their own):
+  1. router logits [N, E] ~ N(0, 1)            (child 0)
+  2. activations x [N, H] ~ N(0, 1)            (child 1)
+  3. W1[e] [2I, H] ~ N(0, 0.02^2), e = 0..L-1  (child 2, grandchild e)
+  4. W2[e] [H, I]  ~ N(0, 0.02^2), e = 0..L-1  (child 3, grandchild e)
+The skewed workload adds a per-expert bias 1.5 * ln p(e) to the logits, where
+p is a Zipf(s=1.2) popularity over ranks 1..E and global expert e has rank
+e + 1 (index order is popularity order, so the experts 0..L-1 owned by this
+GPU are the hottest ones).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "get_workload", "MoeInputs", "make_inputs",
+    "f32_to_bf16_bits", "quantize_e4m3_blocks", "e4m3_encode",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    num_slices: int          # S: source slices (stand-ins for the EP ranks)
+    tokens_per_slice: int    # T
+    num_experts: int         # E: global experts
+    top_k: int               # k
+    local_begin: int         # e0: first local expert
+    num_local: int           # L: local experts on this GPU
+    hidden: int              # H
+    inter: int               # I
+    dtype: str               # "bf16" or "fp8" (e4m3 with fp32 block scales)
+    skew: bool               # Zipf-biased router logits
+    seed: int
+
+    @property
+    def num_tokens(self) -> int:
+        return self.num_slices * self.tokens_per_slice
+
+    def with_tokens(self, tokens_per_slice: int, name: str | None = None) -> "Workload":
+        return dataclasses.replace(self, tokens_per_slice=tokens_per_slice,
+                                   name=name or f"{self.name}@T{tokens_per_slice}")
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny", 8, 32, 32, 2, 0, 4, 256, 128, "bf16", False, 1001),
+        Workload("dsv3", 8, 512, 256, 8, 0, 32, 7168, 2048, "bf16", False, 1002),
+        Workload("dsv3_skew", 8, 2048, 256, 8, 0, 32, 7168, 2048, "bf16", True, 1003),
+        Workload("dsv3_fp8", 8, 4096, 256, 8, 0, 32, 7168, 2048, "fp8", False, 1004),
+        Workload("qwen3_decode", 8, 16, 128, 8, 0, 16, 4096, 1536, "bf16", False, 1005),
+        Workload("qwen3_prefill", 8, 8192, 128, 8, 0, 16, 4096, 1536, "bf16", False, 1006),
+    ]
+}
+
+
+def get_workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even) and return
+    the 16-bit patterns as uint16. Inputs are finite by construction."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Encode fp32 values as OCP FP8 E4M3 (the 'fn' variant: bias 7, no
+    infinities, 0x7F/0xFF are NaN, largest finite 448), rounding to nearest
+    with ties to even and saturating to +-448. Returns uint8 codes."""
+    v = np.asarray(v, dtype=np.float32)
+    sign = (np.signbit(v)).astype(np.uint8) << np.uint8(7)
+    a = np.minimum(np.abs(v).astype(np.float64), 448.0)
+    # exponent of the binade the value falls in, clamped to the normal range;
+    # below 2^-6 the spacing is the subnormal step 2^-9.
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    e = np.clip(e, -6, 8)
+    step = 2.0 ** (e - 3)
+    q = np.rint(a / step) * step          # np.rint rounds ties to even
+    # rounding can carry into the next binade; recompute fields from q
+    q = np.minimum(q, 448.0)
+    code = np.zeros(v.shape, dtype=np.uint8)
+    nz = q > 0
+    qe = np.floor(np.log2(np.where(nz, q, 1.0)))
+    normal = nz & (qe >= -6)
+    sub = nz & ~normal
+    mant_n = np.rint(q / 2.0 ** qe * 8.0 - 8.0).astype(np.int64)
+    exp_n = (qe + 7).astype(np.int64)
+    code = np.where(normal, (exp_n << 3) | mant_n, 0)
+    code = np.where(sub, np.rint(q / 2.0 ** -9).astype(np.int64), code)
+    return (code.astype(np.uint8) | sign)
+
+
+def quantize_e4m3_blocks(a: np.ndarray, block_rows: int, block_cols: int):
+    """Blockwise e4m3 quantization of a 2-D fp32 array: one fp32 scale per
+    (block_rows x block_cols) block, scale = amax / 448, codes = e4m3(a/scale).
+    Returns (codes uint8 [R, C], scales fp32 [ceil(R/br), ceil(C/bc)])."""
+    a = np.asarray(a, dtype=np.float32)
+    R, C = a.shape
+    assert R % block_rows == 0 and C % block_cols == 0
+    blk = a.reshape(R // block_rows, block_rows, C // block_cols, block_cols)
+    amax = np.abs(blk).max(axis=(1, 3)).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = blk / scale[:, None, :, None]
+    codes = e4m3_encode(q.reshape(R, C))
+    return codes, scale
+
+
+@dataclasses.dataclass
+class MoeInputs:
+    wl: Workload
+    logits: np.ndarray            # fp32 [N, E]
+    bias: np.ndarray | None       # fp32 [E] or None
+    x: np.ndarray                 # bf16 bits uint16 [N, H], or e4m3 codes uint8 [N, H]
+    x_scale: np.ndarray | None    # fp32 [N, H/128] (fp8 only)
+    w1: np.ndarray                # [L, 2I, H] bf16 bits or e4m3 codes
+    w1_scale: np.ndarray | None   # fp32 [L, 2I/128, H/128] (fp8 only)
+    w2: np.ndarray                # [L, H, I]
+    w2_scale: np.ndarray | None   # fp32 [L, H/128, I/128] (fp8 only)
+
+
+def _children(seed: int):
+    ss = np.random.SeedSequence(seed)
+    return ss.spawn(4)
+
+
+def zipf_bias(num_experts: int, s: float = 1.2, strength: float = 1.5) -> np.ndarray:
+    ranks = np.arange(1, num_experts + 1, dtype=np.float64)
+    p = ranks ** (-s)
+    p /= p.sum()
+    return (strength * np.log(p)).astype(np.float32)
+
+
+def _normal(ss, shape, scale=1.0):
+    g = np.random.default_rng(ss)
+    out = g.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        out *= np.float32(scale)
+    return out
+
+
+def make_logits(wl: Workload) -> tuple[np.ndarray, np.ndarray | None]:
+    ch = _children(wl.seed)
+    logits = _normal(ch[0], (wl.num_tokens, wl.num_experts))
+    bias = zipf_bias(wl.num_experts) if wl.skew else None
+    return logits, bias
+
+
+def make_x(wl: Workload):
+    ch = _children(wl.seed)
+    x = _normal(ch[1], (wl.num_tokens, wl.hidden))
+    if wl.dtype == "fp8":
+        return quantize_e4m3_blocks(x, 1, 128)
+    return f32_to_bf16_bits(x), None
+
+
+def make_expert_weights(wl: Workload, e: int):
+    """Weights of local expert e (0-based within the local range)."""
+    ch = _children(wl.seed)
+    s1 = ch[2].spawn(wl.num_local)[e]
+    s2 = ch[3].spawn(wl.num_local)[e]
+    w1 = _normal(s1, (2 * wl.inter, wl.hidden), 0.02)
+    w2 = _normal(s2, (wl.hidden, wl.inter), 0.02)
+    if wl.dtype == "fp8":
+        q1, s1_ = quantize_e4m3_blocks(w1, 128, 128)
+        q2, s2_ = quantize_e4m3_blocks(w2, 128, 128)
+        return q1, s1_, q2, s2_
+    return f32_to_bf16_bits(w1), None, f32_to_bf16_bits(w2), None
+
+
+def make_inputs(wl: Workload, experts: int | None = None) -> MoeInputs:
+    """Generate every input of a workload. ``experts`` limits how many local
+    experts' weights are drawn (the rest are left zero) for quick host tests."""
+    logits, bias = make_logits(wl)
+    x, xs = make_x(wl)
+    L = wl.num_local
+    wdt = np.uint8 if wl.dtype == "fp8" else np.uint16
+    w1 = np.zeros((L, 2 * wl.inter, wl.hidden), dtype=wdt)
+    w2 = np.zeros((L, wl.hidden, wl.inter), dtype=wdt)
+    w1s = w2s = None
+    if wl.dtype == "fp8":
+        w1s = np.ones((L, 2 * wl.inter // 128, wl.hidden // 128), dtype=np.float32)
+        w2s = np.ones((L, wl.hidden // 128, wl.inter // 128), dtype=np.float32)
+    for e in range(L if experts is None else min(experts, L)):
+        a, a_s, b, b_s = make_expert_weights(wl, e)
+        w1[e] = a
+        w2[e] = b
+        if w1s is not None:
+            w1s[e] = a_s
+            w2s[e] = b_s
+    return MoeInputs(wl, logits, bias, x, xs, w1, w1s, w2, w2s)
