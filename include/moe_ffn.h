@@ -1,0 +1,211 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) persistent MoE expert-FFN library.
+ *
+ * One GPU's expert-parallel share of a Mixture-of-Experts FFN layer, as the
+ * X-Stage paper describes DeepGEMM's MegaMoE kernel (section 2.2, "MegaMoE
+ * Execution"; section 4.2, "Capacity-Aware Scheduling across Expert Waves"):
+ *
+ *   routing + dispatch layout  ->  moe_dispatch_layout
+ *   persistent grouped GEMM    ->  moe_ffn_forward: for every local expert,
+ *       Linear-1 (gate and up projections) with the SwiGLU activation fused
+ *       into its epilogue, then Linear-2 (down projection) whose epilogue
+ *       multiplies each row by its router weight and stores it into the
+ *       combine buffer of the source slice the token came from; tiles run
+ *       in the Expert-Wave order or in the paper's Interleaved order
+ *       (Algorithm 1).
+ *   combine audit + reduction  ->  moe_combine_check
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller, unless a
+ *    comment says "host". The library never allocates memory in a call and
+ *    keeps no state besides cached device properties.
+ *  - Every call is enqueued on `stream` (a hipStream_t; NULL means the
+ *    default stream) and returns without waiting for the GPU.
+ *  - Return value: MOE_OK (0) or a negative moe_status. Argument errors are
+ *    detected on the host, before anything is enqueued. Errors found while
+ *    the kernels run (a dependency wait that exceeded its time limit) are
+ *    written to the device status word given in moe_sched_params.status and
+ *    are readable after the stream has been synchronised.
+ *  - Token numbering: source slice s holds tokens_per_slice (T) tokens; the
+ *    global token index is n = s*T + t. Flat pair index f = n*k + j names
+ *    top-k slot j of token n.
+ *  - Layouts are row-major; sizes are in elements unless stated.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_ABI_VERSION 1
+#define MOE_MAX_SLICES 64
+#define MOE_MAX_LOCAL_EXPERTS 256
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,        /* a size, pointer or parameter is invalid */
+  MOE_ERR_UNSUPPORTED = -2,        /* valid, but no kernel handles this shape */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_HIP = -4,                /* a HIP runtime call failed */
+  MOE_ERR_TIMEOUT = -5,            /* device status: a dependency wait timed out */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 } moe_dtype;
+
+typedef enum { MOE_SCHED_EXPERT_WAVE = 0, MOE_SCHED_INTERLEAVED = 1 } moe_schedule;
+
+/* Problem shape. Global experts are 0..num_experts-1; this GPU owns
+ * local_expert_begin .. local_expert_begin+num_local_experts-1. */
+typedef struct {
+  int32_t num_slices;          /* S: source slices (one per EP rank), 1..MOE_MAX_SLICES */
+  int32_t tokens_per_slice;    /* T */
+  int32_t num_experts;         /* E: global experts, 1..1024 */
+  int32_t top_k;               /* k: experts per token, 1..min(E, 16) */
+  int32_t local_expert_begin;  /* e0 */
+  int32_t num_local_experts;   /* L, 1..MOE_MAX_LOCAL_EXPERTS */
+  int32_t hidden;              /* H, a multiple of 128 */
+  int32_t inter;               /* I, a multiple of 128 */
+  int32_t dtype;               /* moe_dtype of x and the weights */
+} moe_shape;
+
+/* Dispatch layout (device arrays, caller-allocated; sizes from the shape,
+ * N = S*T tokens, L local experts, R <= N*k routed rows).
+ * Rows of local expert e are rows row_offset[e] .. row_offset[e+1]-1, in
+ * ascending flat pair index. Scheduler rows (the M-blocks of the grouped
+ * GEMM, the X-Stage paper's rows p with first row O_e per expert in
+ * Algorithm 1) of expert e are tile_offset[e] .. tile_offset[e+1]-1, with
+ * ceil(M_e / block_m) blocks per expert. */
+typedef struct {
+  int32_t* topk_idx;     /* [N, k] global expert of each slot (input when logits == NULL) */
+  float* topk_w;         /* [N, k] router weight of each slot (same)                        */
+  int32_t* counts;       /* [L]    routed rows per local expert (M_e)                       */
+  int32_t* row_offset;   /* [L+1]  exclusive prefix sum of counts                           */
+  int32_t* tile_offset;  /* [L+1]  exclusive prefix sum of ceil(M_e / block_m)              */
+  int32_t* row_pair;     /* [N*k]  flat pair f of each routed row (first R entries valid)   */
+  float* row_weight;     /* [N*k]  router weight of each routed row (first R valid)         */
+  int32_t* pair_row;     /* [N*k]  routed row of pair f, or -1 when its expert is not local */
+  int32_t* totals;       /* [4]    R, P (scheduler rows), max M_e, experts with M_e > 0     */
+  int32_t* scratch;      /* moe_layout_scratch_bytes() bytes of scratch                     */
+  int32_t block_m;       /* M-block size the FFN will use: moe_ffn_plan().block_m           */
+} moe_layout;
+
+/* Scheduling parameters. Zero fields select the automatic choice; an
+ * explicit value always wins. */
+typedef struct {
+  int32_t schedule;          /* moe_schedule                                                */
+  int32_t lead_d;            /* Interleaved lead D in scheduler rows, >= 1; 0 = the
+                                X-Stage paper's anti-starvation knee, Eq. 16               */
+  int32_t experts_per_wave;  /* Expert-Wave group size; 0 = close a wave once it holds at
+                                least one Linear-1 tile per persistent workgroup           */
+  int32_t grid;              /* persistent workgroups G; 0 = all that can be co-resident   */
+  int32_t tile;              /* tile configuration id (moe_ffn_plan); 0 = automatic        */
+  int32_t timeout_ms;        /* dependency-wait limit; 0 = 2000 ms                         */
+  int32_t* status;           /* device int32, or NULL: set to MOE_ERR_TIMEOUT by a wait
+                                that gave up (never cleared by the library)                */
+  uint32_t* trace;           /* device [grid][trace_capacity][2] task records, or NULL:
+                                word 0 = kind (1 = Linear-1, 2 = Linear-2) | n << 2,
+                                word 1 = scheduler row p; unused records stay untouched    */
+  int32_t trace_capacity;    /* records per workgroup                                      */
+  int32_t debug_skip_l1_row; /* testing only: when >= 0, Linear-1 tiles of this scheduler
+                                row are not run, so its Linear-2 waits time out            */
+} moe_sched_params;
+
+/* Resolved plan for a shape and parameters. */
+typedef struct {
+  int32_t tile;        /* tile configuration id                         */
+  int32_t block_m;     /* tokens per M-block (b_m)                      */
+  int32_t block_n1;    /* Linear-1 N-tile width over the 2I gate/up outputs */
+  int32_t block_n2;    /* Linear-2 N-tile width over the H outputs      */
+  int32_t n1_tiles;    /* N1 = 2I / block_n1                            */
+  int32_t n2_tiles;    /* N2 = H / block_n2                             */
+  int32_t grid;        /* persistent workgroups G                       */
+  int32_t lead_d;      /* resolved D                                    */
+  int32_t max_sched_rows;    /* upper bound of P for this shape          */
+  size_t workspace_bytes;    /* bytes moe_ffn_forward needs              */
+} moe_plan;
+
+/* Library version (MOE_FFN_ABI_VERSION). */
+int32_t moe_abi_version(void);
+
+/* Text for a moe_status value (static storage). */
+const char* moe_status_string(int32_t status);
+
+/* Bytes of layout scratch (moe_layout.scratch) for this shape. */
+size_t moe_layout_scratch_bytes(const moe_shape* shape);
+
+/* Resolve tile configuration, grid and lead for a shape on the current
+ * device. Returns MOE_ERR_UNSUPPORTED when no kernel handles the shape. */
+int32_t moe_ffn_plan(const moe_shape* shape, const moe_sched_params* params, moe_plan* plan);
+
+/* Zero a workspace before its first use (moe_ffn_forward leaves it zeroed
+ * again when it completes, so this is needed only once per allocation). */
+int32_t moe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Routing and dispatch layout (the MegaMoE paper's Dispatch stage run
+ * locally; the X-Stage paper, section 2.2, and Algorithm 1's row space).
+ *   logits      [N, E] fp32 router logits, or NULL: then layout->topk_idx
+ *               and layout->topk_w are inputs and routing is skipped.
+ *   expert_bias [E] fp32 added to every token's logits before selection and
+ *               softmax, or NULL.
+ * Routing: z = logits + bias (fp32); the k largest z in descending order,
+ * equal values broken by the lower expert index; weights are the softmax of
+ * the k kept z values. Layout: see moe_layout. Everything stays on the
+ * device; nothing is copied to the host. */
+int32_t moe_dispatch_layout(const moe_shape* shape, const float* logits,
+                            const float* expert_bias, const moe_layout* layout,
+                            void* stream);
+
+/* Persistent fused expert FFN (X-Stage paper, section 2.2 and Algorithm 1).
+ *   x_slices       host array [S] of device pointers, each [T, H] of bf16
+ *                  (MOE_BF16) or e4m3 bytes (MOE_FP8_E4M3).
+ *   x_scales       fp8 only: host array [S] of device pointers, each
+ *                  [T, H/128] fp32 (one scale per 1x128 block); else NULL.
+ *   w1             [L, 2I, H]: rows 0..I-1 of expert e are the gate
+ *                  projection, rows I..2I-1 the up projection.
+ *   w1_scales      fp8 only: [L, 2I/128, H/128] fp32 per 128x128 block.
+ *   w2             [L, H, I] down projection.
+ *   w2_scales      fp8 only: [L, H/128, I/128] fp32.
+ *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
+ *                  Slot (t, j) of slice s receives
+ *                     bf16( w[n, j] * FFN_e(x[n]) ),  n = s*T + t,
+ *                  for every pair whose expert e is local; other slots are
+ *                  not touched.
+ *   workspace      moe_ffn_plan().workspace_bytes bytes, zeroed once with
+ *                  moe_workspace_init.
+ * The layout must come from moe_dispatch_layout with layout->block_m equal
+ * to moe_ffn_plan().block_m for the same shape and parameters. */
+int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
+                        const void* const* x_slices, const float* const* x_scales,
+                        const void* w1, const float* w1_scales,
+                        const void* w2, const float* w2_scales,
+                        void* const* combine_slices,
+                        void* workspace, size_t workspace_bytes,
+                        const moe_sched_params* params, void* stream);
+
+/* Combine audit and source-side reduction (the "aggregate the top-k
+ * results" half of Combine, X-Stage paper, section 2.2).
+ *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
+ *   y_local        [N, H] fp32 or NULL: y_local[n] = sum over the local
+ *                  slots j of token n, in ascending j, of combine[n, j].
+ *   report         device int32 [4] or NULL; counts are ADDED to it:
+ *                  [0] local slots still holding the sentinel 0xFFFF in
+ *                      their first element (never written),
+ *                  [1] non-local slots whose first element is not the
+ *                      sentinel (written although not local),
+ *                  [2] non-finite values in local slots,
+ *                  [3] unused (0).
+ *                  The audit reads every slot; pass NULL to skip it. */
+int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,
+                          void* const* combine_slices, float* y_local,
+                          int32_t* report, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

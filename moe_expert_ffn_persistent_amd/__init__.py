@@ -1,0 +1,148 @@
+"""MI355X (gfx950) persistent MoE expert FFN: Python binding.
+
+PyTorch serves only as the device allocator and stream provider: every step
+(routing, dispatch layout, Linear-1 + SwiGLU, Linear-2 + weighted combine
+stores, combine reduction) runs in the HIP kernels of libmoe_ffn.so through
+its C ABI (include/moe_ffn.h). If the library is missing, every call raises;
+there is no host fallback.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_BF16, MOE_FP8_E4M3, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED,
+                   MoeError, MoeLayout, MoePlan, MoeSchedParams, MoeShape)
+
+__all__ = ["MoeExpertFFN", "LayoutBuffers", "MoeError", "SCHEDULES", "make_shape",
+           "make_params", "library"]
+
+SCHEDULES = {"expert_wave": MOE_SCHED_EXPERT_WAVE, "interleaved": MOE_SCHED_INTERLEAVED}
+DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+
+
+def library():
+    """The loaded ctypes library (raises if it has not been built)."""
+    return _lib.load()
+
+
+def make_shape(S, T, E, k, e0, L, H, I, dtype="bf16") -> MoeShape:
+    return MoeShape(S, T, E, k, e0, L, H, I, DTYPES[dtype])
+
+
+def make_params(schedule="interleaved", lead_d=0, experts_per_wave=0, grid=0, tile=0,
+                timeout_ms=0, status=None, trace=None, trace_capacity=0,
+                debug_skip_l1_row=-1) -> MoeSchedParams:
+    return MoeSchedParams(SCHEDULES[schedule], lead_d, experts_per_wave, grid, tile, timeout_ms,
+                          None if status is None else status.data_ptr(),
+                          None if trace is None else trace.data_ptr(), trace_capacity,
+                          debug_skip_l1_row)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+@dataclasses.dataclass
+class LayoutBuffers:
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    row_offset: torch.Tensor
+    tile_offset: torch.Tensor
+    row_pair: torch.Tensor
+    row_weight: torch.Tensor
+    pair_row: torch.Tensor
+    totals: torch.Tensor
+    scratch: torch.Tensor
+    block_m: int
+
+    @classmethod
+    def allocate(cls, shape: MoeShape, block_m: int, device) -> "LayoutBuffers":
+        N = shape.num_slices * shape.tokens_per_slice
+        k, L = shape.top_k, shape.num_local_experts
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        nscr = max(1, _lib.layout_scratch_bytes(shape) // 4)
+        return cls(torch.zeros((N, k), **i32), torch.zeros((N, k), **f32),
+                   torch.zeros(L, **i32), torch.zeros(L + 1, **i32), torch.zeros(L + 1, **i32),
+                   torch.zeros(max(1, N * k), **i32), torch.zeros(max(1, N * k), **f32),
+                   torch.zeros(max(1, N * k), **i32), torch.zeros(4, **i32),
+                   torch.zeros(nscr, **i32), block_m)
+
+    def c_struct(self) -> MoeLayout:
+        return MoeLayout(*(t.data_ptr() for t in (
+            self.topk_idx, self.topk_w, self.counts, self.row_offset, self.tile_offset,
+            self.row_pair, self.row_weight, self.pair_row, self.totals, self.scratch)),
+            self.block_m)
+
+
+class MoeExpertFFN:
+    """One GPU's share of an MoE FFN layer: S source slices of T tokens,
+    E global experts with top-k routing, local experts e0..e0+L-1, hidden H,
+    intermediate I. Owns the layout buffers and the workspace; the caller
+    owns inputs, weights and combine buffers."""
+
+    def __init__(self, S, T, E, k, e0, L, H, I, dtype="bf16", schedule="interleaved",
+                 lead_d=0, experts_per_wave=0, grid=0, tile=0, timeout_ms=0, device="cuda"):
+        self.device = torch.device(device)
+        self.shape = make_shape(S, T, E, k, e0, L, H, I, dtype)
+        self.dtype = dtype
+        self.defaults = dict(schedule=schedule, lead_d=lead_d, experts_per_wave=experts_per_wave,
+                             grid=grid, tile=tile, timeout_ms=timeout_ms)
+        with torch.cuda.device(self.device):
+            self.plan = _lib.ffn_plan(self.shape, make_params(**self.defaults))
+            self.layout_bufs = LayoutBuffers.allocate(self.shape, self.plan.block_m, self.device)
+            self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+            self.workspace = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8,
+                                         device=self.device)
+            _lib.workspace_init(self.workspace.data_ptr(), self.plan.workspace_bytes,
+                                _stream(None))
+
+    @property
+    def num_tokens(self) -> int:
+        return self.shape.num_slices * self.shape.tokens_per_slice
+
+    def params(self, **over) -> MoeSchedParams:
+        kw = dict(self.defaults)
+        kw.update(over)
+        kw.setdefault("status", self.status)
+        return make_params(**kw)
+
+    def resolved_plan(self, **over) -> MoePlan:
+        return _lib.ffn_plan(self.shape, self.params(**over))
+
+    def layout(self, logits=None, bias=None, topk_idx=None, topk_w=None, stream=None):
+        """Routing (from fp32 logits [N, E] and optional bias [E]) or given
+        top-k (int32 idx and fp32 weights [N, k]), then the dispatch layout."""
+        lb = self.layout_bufs
+        if logits is None:
+            lb.topk_idx.copy_(topk_idx)
+            lb.topk_w.copy_(topk_w)
+        _lib.dispatch_layout(self.shape, None if logits is None else logits.data_ptr(),
+                             None if bias is None else bias.data_ptr(), lb.c_struct(),
+                             _stream(stream))
+        return lb
+
+    def forward(self, x_slices, w1, w2, combine_slices, x_scales=None, w1_scales=None,
+                w2_scales=None, stream=None, **sched):
+        """Run Linear-1 + SwiGLU and Linear-2 + weighted combine stores for
+        every local expert, in the schedule given by ``sched`` (defaults from
+        the constructor)."""
+        params = self.params(**sched)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        _lib.ffn_forward(self.shape, self.layout_bufs.c_struct(),
+                         [t.data_ptr() for t in x_slices],
+                         None if x_scales is None else [t.data_ptr() for t in x_scales],
+                         w1.data_ptr(), ptr(w1_scales), w2.data_ptr(), ptr(w2_scales),
+                         [t.data_ptr() for t in combine_slices], self.workspace.data_ptr(),
+                         self.plan.workspace_bytes, params, _stream(stream))
+
+    def combine_check(self, combine_slices, y=None, report=None, stream=None):
+        _lib.combine_check(self.shape, self.layout_bufs.c_struct(),
+                           [t.data_ptr() for t in combine_slices],
+                           None if y is None else y.data_ptr(),
+                           None if report is None else report.data_ptr(), _stream(stream))

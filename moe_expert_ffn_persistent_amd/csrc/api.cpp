@@ -1,0 +1,301 @@
+// Host side of the C ABI declared in include/moe_ffn.h: argument checks,
+// tile/grid/lead resolution, workspace carving and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "internal.hpp"
+
+namespace moe {
+
+extern const TileInfo kBf16Tiles[];
+hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s);
+hipError_t occupancy_ffn_bf16(int id, int* n);
+
+namespace {
+
+constexpr int kNumBf16Tiles = 3;
+
+struct DeviceProps {
+  bool ready = false;
+  int cus = 0;
+  int wall_khz = 0;
+  int occ[16] = {};
+};
+
+std::mutex g_mu;
+DeviceProps g_props[64];
+
+int device_props(DeviceProps** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceProps& p = g_props[dev];
+  if (!p.ready) {
+    if (hipDeviceGetAttribute(&p.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(&p.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        p.wall_khz <= 0)
+      p.wall_khz = 100000;
+    for (int id = 1; id <= kNumBf16Tiles; ++id) {
+      int n = 0;
+      if (occupancy_ffn_bf16(id, &n) != hipSuccess) return MOE_ERR_HIP;
+      p.occ[id] = n;
+    }
+    p.ready = true;
+  }
+  *out = &p;
+  return MOE_OK;
+}
+
+bool shape_ok(const moe_shape* s) {
+  if (!s) return false;
+  if (s->num_slices < 1 || s->num_slices > MOE_MAX_SLICES) return false;
+  if (s->tokens_per_slice < 0) return false;
+  if (s->num_experts < 1 || s->num_experts > 1024) return false;
+  if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->num_experts) return false;
+  if (s->num_local_experts < 1 || s->num_local_experts > MOE_MAX_LOCAL_EXPERTS) return false;
+  if (s->local_expert_begin < 0 || s->local_expert_begin + s->num_local_experts > s->num_experts)
+    return false;
+  if (s->hidden < 128 || s->hidden % 128 || s->inter < 128 || s->inter % 128) return false;
+  if (s->dtype != MOE_BF16 && s->dtype != MOE_FP8_E4M3) return false;
+  const long long pairs = (long long)s->num_slices * s->tokens_per_slice * s->top_k;
+  if (pairs > (1ll << 30)) return false;
+  return true;
+}
+
+long long num_tokens(const moe_shape* s) { return (long long)s->num_slices * s->tokens_per_slice; }
+
+const TileInfo* find_tile(int id) {
+  for (int i = 0; i < kNumBf16Tiles; ++i)
+    if (kBf16Tiles[i].id == id) return &kBf16Tiles[i];
+  return nullptr;
+}
+
+bool tile_fits(const TileInfo* t, const moe_shape* s) {
+  return t && t->dtype == s->dtype && s->hidden % t->block_n == 0 && (2 * s->inter) % t->block_n == 0;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct WsLayout {
+  size_t h, hs, l2_full, done, total;
+};
+
+WsLayout carve(const moe_shape* s, int block_m, int max_rows) {
+  WsLayout w{};
+  const size_t rows = (size_t)max_rows * block_m;
+  const size_t elt = s->dtype == MOE_FP8_E4M3 ? 1 : 2;
+  w.h = 0;
+  size_t off = align_up(rows * s->inter * elt, 256);
+  w.hs = off;
+  if (s->dtype == MOE_FP8_E4M3) off = align_up(off + rows * (s->inter / 128) * 4, 256);
+  w.l2_full = off;
+  off = align_up(off + (size_t)max_rows * 4, 256);
+  w.done = off;
+  off += 256;
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char* moe_status_string(int32_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "a Linear-2 tile timed out waiting for its Linear-1 inputs";
+  }
+  return "unknown status";
+}
+
+size_t moe_layout_scratch_bytes(const moe_shape* s) {
+  if (!shape_ok(s)) return 0;
+  const long long pairs = num_tokens(s) * s->top_k;
+  const long long chunks = (pairs + kLayoutChunk - 1) / kLayoutChunk;
+  return (size_t)std::max<long long>(chunks, 1) * s->num_local_experts * 4;
+}
+
+int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* out) {
+  if (!shape_ok(s) || !prm || !out) return MOE_ERR_INVALID_ARG;
+  if (prm->schedule != MOE_SCHED_EXPERT_WAVE && prm->schedule != MOE_SCHED_INTERLEAVED)
+    return MOE_ERR_INVALID_ARG;
+  if (prm->lead_d < 0 || prm->grid < 0 || prm->experts_per_wave < 0 || prm->timeout_ms < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  DeviceProps* dp = nullptr;
+  int st = device_props(&dp);
+  if (st != MOE_OK) return st;
+
+  const TileInfo* t = nullptr;
+  if (prm->tile > 0) {
+    t = find_tile(prm->tile);
+    if (!t) return MOE_ERR_INVALID_ARG;
+    if (!tile_fits(t, s)) return MOE_ERR_UNSUPPORTED;
+  } else {
+    // expected rows per local expert under uniform routing
+    const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
+    const int order_small[] = {3, 1, 2};
+    const int order_large[] = {1, 2, 3};
+    const int* order = avg <= 48.0 ? order_small : order_large;
+    for (int i = 0; i < 3 && !t; ++i)
+      if (tile_fits(find_tile(order[i]), s)) t = find_tile(order[i]);
+    if (!t) return MOE_ERR_UNSUPPORTED;
+  }
+  const int capacity = dp->occ[t->id] * dp->cus;
+  if (capacity < 1) return MOE_ERR_UNSUPPORTED;
+  int grid = capacity;
+  if (prm->grid > 0) {
+    if (prm->grid > capacity) return MOE_ERR_INVALID_ARG;   // all workgroups must be co-resident
+    grid = prm->grid;
+  }
+  moe_plan p{};
+  p.tile = t->id;
+  p.block_m = t->block_m;
+  p.block_n1 = t->block_n;
+  p.block_n2 = t->block_n;
+  p.n1_tiles = 2 * s->inter / t->block_n;
+  p.n2_tiles = s->hidden / t->block_n;
+  p.grid = grid;
+  // X-Stage paper, Eq. 16: rows spanned by G concurrently running Linear-1 tiles
+  p.lead_d = prm->lead_d > 0 ? prm->lead_d : std::max(1, (grid + p.n1_tiles - 1) / p.n1_tiles);
+  const long long pairs = num_tokens(s) * s->top_k;
+  long long rows = (pairs + (long long)s->num_local_experts * (t->block_m - 1)) / t->block_m;
+  p.max_sched_rows = (int)std::max<long long>(rows, 1);
+  p.workspace_bytes = carve(s, p.block_m, p.max_sched_rows).total;
+  *out = p;
+  return MOE_OK;
+}
+
+int32_t moe_workspace_init(void* ws, size_t bytes, void* stream) {
+  if (!ws && bytes) return MOE_ERR_INVALID_ARG;
+  return launch_zero(ws, bytes, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int32_t moe_dispatch_layout(const moe_shape* s, const float* logits, const float* bias,
+                            const moe_layout* lay, void* stream) {
+  if (!shape_ok(s) || !lay) return MOE_ERR_INVALID_ARG;
+  if (lay->block_m < 1) return MOE_ERR_INVALID_ARG;
+  if (!lay->counts || !lay->row_offset || !lay->tile_offset || !lay->totals || !lay->scratch)
+    return MOE_ERR_INVALID_ARG;
+  if (num_tokens(s) > 0 && (!lay->topk_idx || !lay->topk_w || !lay->row_pair || !lay->row_weight ||
+                            !lay->pair_row))
+    return MOE_ERR_INVALID_ARG;
+  LayoutArgs a{};
+  a.N = (int)num_tokens(s);
+  a.E = s->num_experts;
+  a.k = s->top_k;
+  a.e0 = s->local_expert_begin;
+  a.L = s->num_local_experts;
+  a.block_m = lay->block_m;
+  a.logits = logits;
+  a.bias = bias;
+  a.topk_idx = lay->topk_idx;
+  a.topk_w = lay->topk_w;
+  a.counts = lay->counts;
+  a.row_offset = lay->row_offset;
+  a.tile_offset = lay->tile_offset;
+  a.row_pair = lay->row_pair;
+  a.row_weight = lay->row_weight;
+  a.pair_row = lay->pair_row;
+  a.totals = lay->totals;
+  a.block_counts = lay->scratch;
+  a.nchunks = (int)(((long long)a.N * a.k + kLayoutChunk - 1) / kLayoutChunk);
+  return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* const* x_slices,
+                        const float* const* x_scales, const void* w1, const float* w1_scales,
+                        const void* w2, const float* w2_scales, void* const* comb, void* ws,
+                        size_t ws_bytes, const moe_sched_params* prm, void* stream) {
+  if (!shape_ok(s) || !lay || !prm || !x_slices || !comb || !w1 || !w2 || !ws)
+    return MOE_ERR_INVALID_ARG;
+  (void)x_scales;
+  (void)w1_scales;
+  (void)w2_scales;
+  moe_plan plan{};
+  int st = moe_ffn_plan(s, prm, &plan);
+  if (st != MOE_OK) return st;
+  if (lay->block_m != plan.block_m) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < plan.workspace_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!lay->row_offset || !lay->tile_offset || !lay->row_pair || !lay->row_weight)
+    return MOE_ERR_INVALID_ARG;
+  if (prm->trace && prm->trace_capacity < 1) return MOE_ERR_INVALID_ARG;
+  if (num_tokens(s) == 0) return MOE_OK;
+  for (int i = 0; i < s->num_slices; ++i)
+    if (!x_slices[i] || !comb[i]) return MOE_ERR_INVALID_ARG;
+  DeviceProps* dp = nullptr;
+  st = device_props(&dp);
+  if (st != MOE_OK) return st;
+
+  const WsLayout w = carve(s, plan.block_m, plan.max_sched_rows);
+  FfnArgs a{};
+  a.S = s->num_slices;
+  a.T = s->tokens_per_slice;
+  a.k = s->top_k;
+  a.L = s->num_local_experts;
+  a.H = s->hidden;
+  a.I = s->inter;
+  a.N1 = plan.n1_tiles;
+  a.N2 = plan.n2_tiles;
+  a.grid = plan.grid;
+  a.schedule = prm->schedule;
+  a.lead_d = plan.lead_d;
+  a.experts_per_wave = prm->experts_per_wave;
+  a.debug_skip_row = prm->debug_skip_l1_row;
+  a.trace_cap = prm->trace ? prm->trace_capacity : 0;
+  a.timeout_ticks = (long long)(prm->timeout_ms > 0 ? prm->timeout_ms : 2000) * dp->wall_khz;
+  for (int i = 0; i < s->num_slices; ++i) {
+    a.x[i] = x_slices[i];
+    a.xs[i] = x_scales ? x_scales[i] : nullptr;
+    a.comb[i] = comb[i];
+  }
+  a.w1 = w1;
+  a.w1s = w1_scales;
+  a.w2 = w2;
+  a.w2s = w2_scales;
+  a.row_offset = lay->row_offset;
+  a.tile_offset = lay->tile_offset;
+  a.row_pair = lay->row_pair;
+  a.row_weight = lay->row_weight;
+  char* base = static_cast<char*>(ws);
+  a.h = base + w.h;
+  a.hs = reinterpret_cast<float*>(base + w.hs);
+  a.l2_full = reinterpret_cast<int32_t*>(base + w.l2_full);
+  a.done = reinterpret_cast<int32_t*>(base + w.done);
+  a.status = prm->status;
+  a.trace = prm->trace;
+  return launch_ffn_bf16(plan.tile, a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, float* y,
+                          int32_t* report, void* stream) {
+  if (!shape_ok(s) || !lay || !lay->pair_row || !comb) return MOE_ERR_INVALID_ARG;
+  CheckArgs a{};
+  a.S = s->num_slices;
+  a.T = s->tokens_per_slice;
+  a.k = s->top_k;
+  a.H = s->hidden;
+  a.L = s->num_local_experts;
+  for (int i = 0; i < s->num_slices; ++i) {
+    if (!comb[i] && a.T > 0) return MOE_ERR_INVALID_ARG;
+    a.comb[i] = comb[i];
+  }
+  a.pair_row = lay->pair_row;
+  a.y = y;
+  a.report = report;
+  return launch_check(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Combine audit and source-side reduction for gfx950.
+//
+// After the fused kernel, each source slice holds one bf16 row per
+// (token, top-k slot); the X-Stage paper's Combine then aggregates the top-k
+// results of each token (section 2.2). This kernel does that aggregation for
+// the slots this GPU owns (y_local[n] = sum over local j, ascending j, in
+// fp32) and, optionally, audits the buffers against the 0xFFFF sentinel the
+// caller filled them with: every local slot must have been written, and no
+// other slot may have been touched.
+//
+// One workgroup per token; each thread owns 8 consecutive hidden elements
+// (one 16-byte load per slot), so the reads of a slot are fully coalesced.
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
+  __shared__ int s_cnt[3];
+  const int n = blockIdx.x;
+  const int s = n / a.T;
+  const int t = n - s * a.T;
+  const bool audit = a.report != nullptr;
+  if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  int unwritten = 0, clobbered = 0, nonfinite = 0;
+  const char* base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
+  for (int c = threadIdx.x; c < a.H / 8; c += kThreads) {
+    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < a.k; ++j) {
+      const bool local = a.pair_row[(size_t)n * a.k + j] >= 0;
+      if (!local && !audit) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + ((size_t)j * a.H + c * 8) * 2);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const float f = __uint_as_float(bits << 16);
+        if (local) {
+          y[i] += f;
+          if (audit) {
+            if (bits == 0xFFFFu) unwritten |= 1 << j;
+            else if (!isfinite(f)) nonfinite |= 1 << j;
+          }
+        } else if (bits != 0xFFFFu) {
+          clobbered |= 1 << j;
+        }
+      }
+    }
+    if (a.y) {
+      float4* dst = reinterpret_cast<float4*>(a.y + (size_t)n * a.H + c * 8);
+      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+  if (audit) {
+    // per-slot flags (bit j), merged over the workgroup, then counted
+    atomicOr(&s_cnt[0], unwritten);
+    atomicOr(&s_cnt[1], clobbered);
+    atomicOr(&s_cnt[2], nonfinite);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (s_cnt[0]) atomicAdd(a.report + 0, __popc(s_cnt[0]));
+      if (s_cnt[1]) atomicAdd(a.report + 1, __popc(s_cnt[1]));
+      if (s_cnt[2]) atomicAdd(a.report + 2, __popc(s_cnt[2]));
+    }
+  }
+}
+
+__global__ void zero_words(uint32_t* p, size_t words) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream) {
+  const int N = a.S * a.T;
+  if (N > 0) combine_check<<<N, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  if (words) {
+    const size_t blocks = (words + 255) / 256;
+    zero_words<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(static_cast<uint32_t*>(p), words);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

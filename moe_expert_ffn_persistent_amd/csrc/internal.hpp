@@ -1,0 +1,87 @@
+// Internal declarations shared by the host API and the kernel launchers of
+// the persistent MoE expert-FFN library. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+
+namespace moe {
+
+// Arguments of the layout kernels.
+struct LayoutArgs {
+  int N, E, k, e0, L, block_m;
+  const float* logits;     // [N, E] or nullptr
+  const float* bias;       // [E] or nullptr
+  int32_t* topk_idx;       // [N, k]
+  float* topk_w;           // [N, k]
+  int32_t* counts;         // [L]
+  int32_t* row_offset;     // [L+1]
+  int32_t* tile_offset;    // [L+1]
+  int32_t* row_pair;       // [N*k]
+  float* row_weight;       // [N*k]
+  int32_t* pair_row;       // [N*k]
+  int32_t* totals;         // [4]
+  int32_t* block_counts;   // [nchunks, L]
+  int nchunks;
+};
+
+constexpr int kLayoutChunk = 1024;   // flat pairs per layout workgroup
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+// Arguments of the persistent FFN kernel. Passed by value; the slice tables
+// are copied to LDS at kernel start.
+struct FfnArgs {
+  int S, T, k, L, H, I;
+  int N1, N2;              // Linear-1 / Linear-2 N-tiles per scheduler row
+  int grid;                // persistent workgroups (== gridDim.x)
+  int schedule;            // moe_schedule
+  int lead_d;              // Interleaved lead D (>= 1)
+  int experts_per_wave;    // 0 = greedy
+  int debug_skip_row;      // -1 = off
+  int trace_cap;
+  long long timeout_ticks; // wall-clock ticks before a wait gives up
+  const void* x[MOE_MAX_SLICES];
+  const float* xs[MOE_MAX_SLICES];
+  void* comb[MOE_MAX_SLICES];
+  const void* w1;
+  const float* w1s;
+  const void* w2;
+  const float* w2s;
+  const int32_t* row_offset;
+  const int32_t* tile_offset;
+  const int32_t* row_pair;
+  const float* row_weight;
+  void* h;                 // [P_cap * block_m, I] intermediate activations
+  float* hs;               // fp8: [P_cap * block_m, I/128] scales
+  int32_t* l2_full;        // [P_cap] finished Linear-1 tiles per row
+  int32_t* done;           // [1] finished workgroups
+  int32_t* status;         // device status word or nullptr
+  uint32_t* trace;         // task trace or nullptr
+};
+
+// Tile configurations. Each id maps to one kernel instantiation.
+struct TileInfo {
+  int id;
+  int dtype;       // moe_dtype
+  int block_m;     // tokens per M-block
+  int block_n;     // features per N-tile (both GEMMs)
+  int threads;
+};
+
+
+struct CheckArgs {
+  int S, T, k, H, L;
+  void* comb[MOE_MAX_SLICES];
+  const int32_t* pair_row;
+  float* y;
+  int32_t* report;
+};
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,234 @@
+// Routing and dispatch layout kernels for gfx950.
+//
+// The fused MoE kernel of the X-Stage paper (section 2.2) starts after the
+// router: Dispatch brings each token to the GPU owning its expert, and the
+// grouped GEMM walks a flattened row space in which expert e owns scheduler
+// rows O_e .. O_{e+1}-1 (Algorithm 1 legend). On one GPU the Dispatch stage
+// becomes this layout: which (token, slot) pairs are local, how many rows
+// each local expert gets, their order and their offsets. All of it is
+// integer work except the router softmax, and it must be bit-exact.
+//
+// Kernels, all launched on the caller's stream, no host round trip:
+//   route_topk    one wavefront per token: k rounds of a wavefront argmax
+//                 over (z desc, index asc), softmax over the kept z.
+//   layout_count  one wavefront per chunk of 1024 flat pairs: per-expert
+//                 counts of the chunk.
+//   layout_scan   one workgroup: wavefront prefix scans over the chunk
+//                 counts of each expert (chunk bases), then over experts
+//                 (row and scheduler-row offsets) and the totals.
+//   layout_place  one wavefront per chunk: stable placement. Pairs are taken
+//                 64 at a time in flat order; lanes with the same expert are
+//                 grouped with ballots and ranked by the popcount of the
+//                 lower lanes, so rows of an expert keep ascending f.
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ bool better(float za, int ia, float zb, int ib) {
+  return za > zb || (za == zb && ia < ib);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int t = __shfl_up(v, d, kWave);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+constexpr int kMaxPerLane = 16;   // E <= 1024
+
+__global__ void __launch_bounds__(256) route_topk(LayoutArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (n >= a.N) return;
+  float z[kMaxPerLane];
+  const float* row = a.logits + (size_t)n * a.E;
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    float v = -INFINITY;
+    if (e < a.E) {
+      v = row[e];
+      if (a.bias) v = v + a.bias[e];
+    }
+    z[i] = v;
+  }
+  unsigned taken = 0;   // bit i: element i of this lane already selected
+  float myz = 0.f;      // lane j < k keeps the j-th selection
+  int myi = 0;
+  for (int j = 0; j < a.k; ++j) {
+    float bz = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      const int e = lane + i * kWave;
+      if (e < a.E && !(taken & (1u << i)) && better(z[i], e, bz, bi)) {
+        bz = z[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float oz = __shfl_xor(bz, d, kWave);
+      const int oi = __shfl_xor(bi, d, kWave);
+      if (better(oz, oi, bz, bi)) {
+        bz = oz;
+        bi = oi;
+      }
+    }
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == j) {
+      myz = bz;
+      myi = bi;
+    }
+  }
+  // softmax over the kept values; the first selection is the largest
+  const float zmax = __shfl(myz, 0, kWave);
+  const float ex = lane < a.k ? expf(myz - zmax) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, kWave);
+  if (lane < a.k) {
+    a.topk_idx[(size_t)n * a.k + lane] = myi;
+    a.topk_w[(size_t)n * a.k + lane] = ex / sum;
+  }
+}
+
+__global__ void __launch_bounds__(kWave) layout_count(LayoutArgs a) {
+  extern __shared__ int s_cnt[];   // [L]
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.L; e += kWave) s_cnt[e] = 0;
+  __syncthreads();
+  const int total = a.N * a.k;
+  const int f0 = blockIdx.x * kLayoutChunk;
+  const int f1 = min(total, f0 + kLayoutChunk);
+  for (int f = f0 + lane; f < f1; f += kWave) {
+    const int e = a.topk_idx[f] - a.e0;
+    if (e >= 0 && e < a.L) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = lane; e < a.L; e += kWave) a.block_counts[(size_t)blockIdx.x * a.L + e] = s_cnt[e];
+}
+
+__global__ void __launch_bounds__(256) layout_scan(LayoutArgs a) {
+  extern __shared__ int s_tot[];   // [L] per-expert totals
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  // 1) per expert: exclusive scan over chunks, in place
+  for (int e = wave; e < a.L; e += nwaves) {
+    int carry = 0;
+    for (int c0 = 0; c0 < a.nchunks; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = c < a.nchunks ? a.block_counts[(size_t)c * a.L + e] : 0;
+      const int inc = wave_inclusive_scan(v);
+      if (c < a.nchunks) a.block_counts[(size_t)c * a.L + e] = carry + inc - v;
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+    if (lane == 0) s_tot[e] = carry;
+  }
+  __syncthreads();
+  // 2) over experts: row offsets, scheduler-row offsets, totals
+  if (wave == 0) {
+    int row_carry = 0, tile_carry = 0, mx = 0, active = 0;
+    for (int e0 = 0; e0 < a.L; e0 += kWave) {
+      const int e = e0 + lane;
+      const int cnt = e < a.L ? s_tot[e] : 0;
+      const int tiles = (cnt + a.block_m - 1) / a.block_m;
+      const int rinc = wave_inclusive_scan(cnt);
+      const int tinc = wave_inclusive_scan(tiles);
+      if (e < a.L) {
+        a.counts[e] = cnt;
+        a.row_offset[e] = row_carry + rinc - cnt;
+        a.tile_offset[e] = tile_carry + tinc - tiles;
+      }
+      row_carry += __shfl(rinc, kWave - 1, kWave);
+      tile_carry += __shfl(tinc, kWave - 1, kWave);
+      mx = max(mx, wave_max(cnt));
+      active += wave_sum(cnt > 0 ? 1 : 0);
+    }
+    if (lane == 0) {
+      a.row_offset[a.L] = row_carry;
+      a.tile_offset[a.L] = tile_carry;
+      a.totals[0] = row_carry;
+      a.totals[1] = tile_carry;
+      a.totals[2] = mx;
+      a.totals[3] = active;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
+  extern __shared__ int s_base[];   // [L] next row of each expert in this chunk
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.L; e += kWave)
+    s_base[e] = a.row_offset[e] + a.block_counts[(size_t)blockIdx.x * a.L + e];
+  __syncthreads();
+  const int total = a.N * a.k;
+  const int f0 = blockIdx.x * kLayoutChunk;
+  const int f1 = min(total, f0 + kLayoutChunk);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int fb = f0; fb < f1; fb += kWave) {
+    const int f = fb + lane;
+    int e = -1;
+    if (f < f1) {
+      const int g = a.topk_idx[f] - a.e0;
+      if (g >= 0 && g < a.L) e = g;
+      else a.pair_row[f] = -1;
+    }
+    unsigned long long pending = __ballot(e >= 0);
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int le = __shfl(e, leader, kWave);
+      const unsigned long long same = __ballot(e == le);
+      const int base = s_base[le];
+      if (e == le) {
+        const int r = base + __popcll(same & below);
+        a.row_pair[r] = f;
+        a.row_weight[r] = a.topk_w[f];
+        a.pair_row[f] = r;
+      }
+      __syncthreads();
+      if (lane == 0) s_base[le] = base + __popcll(same);
+      __syncthreads();
+      pending &= ~same;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+  if (a.logits && a.N > 0) {
+    const int per_block = 4;   // tokens (wavefronts) per workgroup
+    route_topk<<<(a.N + per_block - 1) / per_block, per_block * kWave, 0, stream>>>(a);
+  }
+  const size_t lds = sizeof(int) * (size_t)a.L;
+  if (a.nchunks > 0) layout_count<<<a.nchunks, kWave, lds, stream>>>(a);
+  layout_scan<<<1, 256, lds, stream>>>(a);
+  if (a.nchunks > 0) layout_place<<<a.nchunks, kWave, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,218 @@
+"""GPU parity of the persistent expert FFN against the oracle.
+
+Bar: every local combine slot within max|err| <= 1e-2 * max|ref| per row
+(bf16), non-local slots untouched, the two schedules bitwise identical, the
+task trace identical to the CPU model of the schedules."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as mo
+from oracle import schedule as sc
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import SENTINEL, Uploaded, dev, make_ffn, row_rel_err, run_forward, to_dev  # noqa: E402
+
+TOL_BF16 = 1e-2
+
+
+def _route_and_layout(ffn, up):
+    return ffn.layout(logits=up.logits, bias=up.bias)
+
+
+def _check_against_oracle(up, ref, tol=TOL_BF16):
+    C = up.combine_f64()
+    bits = up.combine_bits()
+    local = ref.written
+    # untouched non-local slots
+    assert (bits[~local] == 0xFFFF).all(), "non-local slot written"
+    assert not (bits[local] == 0xFFFF).any(), "local slot left unwritten"
+    err = row_rel_err(C[local], ref.C[local])
+    assert np.isfinite(C[local]).all()
+    assert err.max() <= tol, f"max per-row rel err {err.max():.3e}"
+    return err.max()
+
+
+def _small_wl(**kw):
+    base = dict(name="small", num_slices=8, tokens_per_slice=32, num_experts=32, top_k=2,
+                local_begin=0, num_local=4, hidden=256, inter=128, dtype="bf16", skew=False,
+                seed=1001)
+    base.update(kw)
+    return mi.Workload(**base)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_tiny_all_tiles_both_schedules(tile):
+    wl = mi.get_workload("tiny")
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl, tile=tile)
+    print(f"[ffn] tiny tile={tile} plan block_m={ffn.plan.block_m} grid={ffn.plan.grid}", flush=True)
+    _route_and_layout(ffn, up)
+    outs = {}
+    for sched in ("expert_wave", "interleaved"):
+        up.reset_combine()
+        run_forward(ffn, up, schedule=sched)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        _check_against_oracle(up, ref)
+        outs[sched] = up.combine_bits().copy()
+    assert (outs["expert_wave"] == outs["interleaved"]).all()
+
+
+@pytest.mark.parametrize("H,I,T,L,k,E", [(384, 256, 45, 5, 3, 24), (512, 384, 100, 6, 4, 12),
+                                          (256, 640, 7, 3, 2, 6)])
+def test_ragged_shapes(H, I, T, L, k, E):
+    wl = _small_wl(hidden=H, inter=I, tokens_per_slice=T, num_local=L, top_k=k, num_experts=E,
+                   num_slices=3, seed=7000 + H + I)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp, separate_slices=True)
+    for tile in (1, 3):
+        if H % (256 if tile == 1 else 128) or (2 * I) % (256 if tile == 1 else 128):
+            continue
+        ffn = make_ffn(wl, tile=tile)
+        print(f"[ffn] ragged H={H} I={I} T={T} tile={tile}", flush=True)
+        _route_and_layout(ffn, up)
+        for sched in ("expert_wave", "interleaved"):
+            up.reset_combine()
+            run_forward(ffn, up, schedule=sched)
+            torch.cuda.synchronize()
+            _check_against_oracle(up, ref)
+
+
+def test_weights_scale_outputs_exactly():
+    # the router weight multiplies the fp32 accumulator before the single
+    # rounding: doubling every weight doubles every output bit-exactly
+    wl = mi.get_workload("tiny")
+    inp = mi.make_inputs(wl)
+    idx, w = mo.route(inp.logits, None, wl.top_k)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    w32 = w.astype(np.float32)
+    ffn.layout(topk_idx=to_dev(idx), topk_w=to_dev(w32))
+    run_forward(ffn, up)
+    torch.cuda.synchronize()
+    a = up.combine_f64()
+    up.reset_combine()
+    ffn.layout(topk_idx=to_dev(idx), topk_w=to_dev(2 * w32))
+    run_forward(ffn, up)
+    torch.cuda.synchronize()
+    b = up.combine_f64()
+    local = mo.dispatch_layout(idx, 0, wl.num_local, 16).pair_row.reshape(wl.num_tokens, wl.top_k) >= 0
+    assert (b[local] == 2 * a[local]).all()
+
+
+@pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
+@pytest.mark.parametrize("grid,lead,epw", [(1, 1, 0), (3, 1, 1), (5, 2, 0), (7, 100, 2)])
+def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
+    wl = _small_wl(tokens_per_slice=40, num_local=5, num_experts=10, top_k=3, seed=555)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=32)
+    up = Uploaded(inp)
+    cap = 4096
+    trace = torch.full((grid, cap, 2), -1, dtype=torch.int32, device=dev())
+    ffn = make_ffn(wl, tile=3)
+    print(f"[ffn] trace {schedule} grid={grid} D={lead} epw={epw}", flush=True)
+    _route_and_layout(ffn, up)
+    ffn.forward(up.x_slices, up.w1, up.w2, up.comb_slices, schedule=schedule, grid=grid,
+                lead_d=lead, experts_per_wave=epw, trace=trace, trace_capacity=cap)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    _check_against_oracle(up, ref)
+    plan = ffn.resolved_plan(grid=grid, lead_d=lead)
+    tile_offset = ffn.layout_bufs.tile_offset.cpu().numpy().tolist()
+    want = sc.all_streams(schedule, grid, tile_offset, plan.n1_tiles, plan.n2_tiles, lead, epw)
+    tr = trace.cpu().numpy()
+    for g in range(grid):
+        recs = tr[g]
+        used = recs[recs[:, 0] != -1]
+        got = [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used]
+        assert got == want[g], f"instance {g}"
+
+
+def test_watchdog_reports_timeout_instead_of_hanging():
+    wl = mi.get_workload("tiny")
+    inp = mi.make_inputs(wl)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    _route_and_layout(ffn, up)
+    print("[ffn] watchdog: Linear-1 of row 0 withheld, 50 ms limit", flush=True)
+    run_forward(ffn, up, debug_skip_l1_row=0, timeout_ms=50)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == -5
+    # the workspace is clean again: a normal call afterwards is correct
+    ffn.status.zero_()
+    up.reset_combine()
+    run_forward(ffn, up)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    _check_against_oracle(up, mo.run(inp, block_m=16))
+
+
+def test_combine_check_reduce_and_audit():
+    wl = mi.get_workload("tiny")
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    _route_and_layout(ffn, up)
+    run_forward(ffn, up)
+    y = torch.zeros((wl.num_tokens, wl.hidden), dtype=torch.float32, device=dev())
+    report = torch.zeros(4, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, y=y, report=report)
+    torch.cuda.synchronize()
+    assert report.cpu().tolist() == [0, 0, 0, 0]
+    err = row_rel_err(y.cpu().numpy().astype(np.float64), ref.y_local)
+    has = ref.written.any(axis=1)
+    assert err[has].max() <= TOL_BF16
+    assert (y.cpu().numpy()[~has] == 0).all()
+    # plant: clobber a non-local slot and clear a local one
+    nl = np.argwhere(~ref.written)[0]
+    lo = np.argwhere(ref.written)[0]
+    S_T = wl.tokens_per_slice
+    up.comb_all[nl[0] // S_T, nl[0] % S_T, nl[1], 5] = 0
+    up.comb_all[lo[0] // S_T, lo[0] % S_T, lo[1], :] = SENTINEL
+    report.zero_()
+    ffn.combine_check(up.comb_slices, y=None, report=report)
+    torch.cuda.synchronize()
+    assert report.cpu().tolist()[:2] == [1, 1]
+
+
+def test_empty_batch_and_single_token():
+    wl = _small_wl(tokens_per_slice=0)
+    ffn = make_ffn(wl)
+    up = Uploaded(mi.make_inputs(wl))
+    ffn.layout(logits=up.logits)
+    run_forward(ffn, up)
+    torch.cuda.synchronize()
+    wl1 = _small_wl(num_slices=1, tokens_per_slice=1, num_local=32, seed=31)
+    inp = mi.make_inputs(wl1)
+    ref = mo.run(inp, block_m=16)
+    up1 = Uploaded(inp)
+    ffn1 = make_ffn(wl1)
+    _route_and_layout(ffn1, up1)
+    run_forward(ffn1, up1)
+    torch.cuda.synchronize()
+    _check_against_oracle(up1, ref)
+
+
+def test_all_tokens_on_one_expert_many_blocks():
+    wl = _small_wl(tokens_per_slice=300, num_slices=2, num_local=3, top_k=1, seed=77)
+    inp = mi.make_inputs(wl)
+    inp.bias = np.zeros(wl.num_experts, np.float32)
+    inp.bias[1] = 40.0
+    ref = mo.run(inp, block_m=16)
+    assert (ref.layout.counts == [0, 600, 0]).all()
+    up = Uploaded(inp)
+    for tile in (1, 3):
+        ffn = make_ffn(wl, tile=tile)
+        _route_and_layout(ffn, up)
+        for sched in ("expert_wave", "interleaved"):
+            up.reset_combine()
+            run_forward(ffn, up, schedule=sched)
+            torch.cuda.synchronize()
+            _check_against_oracle(up, ref)
