@@ -1,0 +1,276 @@
+"""Benchmark of one GPU's expert-parallel MoE FFN share on MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+routing + dispatch layout (moe_dispatch_layout), the persistent fused FFN
+(moe_ffn_forward: Linear-1 + SwiGLU, Linear-2 + weighted combine stores) and
+the source-side reduction of the combine slots (moe_combine_check with
+y_local). Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line. ``value`` is TFLOP/s of the algorithmic FLOPs
+(6*H*I per routed row) over the whole step, for the schedule named in
+config.schedule; per-schedule FFN-only timings (paired, A-B-B-A order) and
+the roofline of the dominant kernel ride along, with the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import moe_inputs as mi  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FFN_KERNEL = "moe_ffn_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_ffn_persistent_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("ffn") or name == "sched.hpp":
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(wl, R: int, active: int):
+    H, I = wl.hidden, wl.inter
+    flops = 6.0 * H * I * R
+    sw = 1 if wl.dtype == "fp8" else 2
+    weight_bytes = active * 3.0 * H * I * sw
+    x_bytes = R * H * sw
+    h_bytes = 2.0 * R * I * sw
+    comb_bytes = R * H * 2.0
+    scale_bytes = 0.0
+    if wl.dtype == "fp8":
+        scale_bytes = active * 3.0 * (H // 128) * (I // 128) * 4 + R * (H // 128) * 4 \
+            + 2.0 * R * (I // 128) * 4
+    return flops, weight_bytes + x_bytes + h_bytes + comb_bytes + scale_bytes, dict(
+        weights=weight_bytes, x=x_bytes, h=h_bytes, combine=comb_bytes, scales=scale_bytes)
+
+
+def cpu_baseline(inp, seconds_budget: float):
+    """Time the CPU oracle on a bounded sample: routing and layout over all
+    tokens, then the expert FFN and weighted combine for as many local
+    experts (in order) as fit the budget."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as mo
+    wl = inp.wl
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    n_exp = 0
+    rows = 0
+    res = None
+    while n_exp < wl.num_local:
+        n_exp = min(wl.num_local, max(1, n_exp * 2))
+        t1 = time.perf_counter()
+        res = mo.run(inp, block_m=128, experts=n_exp)
+        dt = time.perf_counter() - t1
+        rows = int(res.layout.row_offset[n_exp])
+        if time.perf_counter() - t0 + 2.5 * dt > seconds_budget:
+            break
+    flops = 6.0 * wl.hidden * wl.inter * rows
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{wl.name}: routing+layout of all {wl.num_tokens} tokens, expert FFN and "
+                      f"combine of local experts 0..{n_exp - 1} ({rows} routed rows), float64 "
+                      f"numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--schedule", default="interleaved", choices=["interleaved", "expert_wave"])
+    ap.add_argument("--pairs", type=int, default=10, help="A-B-B-A rounds of the schedule comparison")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--lead-d", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported here "
+              "(one process, one MI355X). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    wl = mi.get_workload(args.workload)
+    t_gen = time.perf_counter()
+    inp = mi.make_inputs(wl, workers=min(16, os.cpu_count() or 1))   # before any GPU call
+    t_gen = time.perf_counter() - t_gen
+
+    import torch
+
+    from moe_expert_ffn_persistent_amd import MoeExpertFFN
+    dev = torch.device("cuda:0")
+    S, T, H, k = wl.num_slices, wl.tokens_per_slice, wl.hidden, wl.top_k
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    logits = up(inp.logits)
+    bias = None if inp.bias is None else up(inp.bias)
+    x = up(inp.x.reshape(S, T, H))
+    xs = None if inp.x_scale is None else up(inp.x_scale.reshape(S, T, H // 128))
+    w1, w2 = up(inp.w1), up(inp.w2)
+    w1s = None if inp.w1_scale is None else up(inp.w1_scale)
+    w2s = None if inp.w2_scale is None else up(inp.w2_scale)
+    comb = torch.empty((S, T, k, H), dtype=torch.int16, device=dev)
+    y = torch.empty((wl.num_tokens, H), dtype=torch.float32, device=dev)
+    x_sl = [x[s] for s in range(S)]
+    xs_sl = None if xs is None else [xs[s] for s in range(S)]
+    c_sl = [comb[s] for s in range(S)]
+
+    ffn = MoeExpertFFN(S, T, wl.num_experts, k, wl.local_begin, wl.num_local, H, wl.inter,
+                       dtype=wl.dtype, schedule=args.schedule, tile=args.tile,
+                       lead_d=args.lead_d, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def ffn_call(schedule):
+        ffn.forward(x_sl, w1, w2, c_sl, x_scales=xs_sl, w1_scales=w1s, w2_scales=w2s,
+                    schedule=schedule)
+
+    def step(schedule, ev=None):
+        ffn.layout(logits=logits, bias=bias)
+        if ev is not None:
+            ev[0].record(stream)
+        ffn_call(schedule)
+        if ev is not None:
+            ev[1].record(stream)
+        ffn.combine_check(c_sl, y=y)
+
+    ffn.layout(logits=logits, bias=bias)
+    torch.cuda.synchronize()
+    totals = ffn.layout_bufs.totals.cpu().numpy()
+    R, P, max_rows, active = (int(v) for v in totals)
+    flops, alg_bytes, byte_parts = algorithmic_counts(wl, R, active)
+
+    for _ in range(args.warmup):
+        step(args.schedule)
+    torch.cuda.synchronize()
+    if int(ffn.status.item()) != 0:
+        raise RuntimeError(f"device status {int(ffn.status.item())} after warm-up")
+
+    # ---- timed region: exactly K steps of the headline schedule ----
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.schedule, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ffn_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    if int(ffn.status.item()) != 0:
+        raise RuntimeError(f"device status {int(ffn.status.item())} in the timed region")
+
+    # ---- paired schedule comparison, FFN only, A-B-B-A ----
+    per = {"expert_wave": [], "interleaved": []}
+    order = ["expert_wave", "interleaved"]
+    for r in range(args.pairs):
+        seq = order if r % 2 == 0 else order[::-1]
+        for sched in seq:
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            ffn_call(sched)
+            b_.record(stream)
+            b_.synchronize()
+            per[sched].append(a_.elapsed_time(b_))
+    sched_out = {}
+    for s_, v in per.items():
+        med = statistics.median(v)
+        sched_out[s_] = {"ffn_us_median": round(med * 1e3, 2), "ffn_us_min": round(min(v) * 1e3, 2),
+                         "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+                         "hbm_gbs": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
+    speedup = statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    plan = ffn.plan
+    peak_flops = PEAK_FP8_TFLOPS if wl.dtype == "fp8" else PEAK_BF16_TFLOPS
+    ffn_avg_s = statistics.mean(ffn_ms) * 1e-3
+    t_mfma = flops / (peak_flops * 1e12)
+    t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE)).get(wl.name)
+            if tr and tr.get("kernel_hash") == kernel_source_hash():
+                traffic = tr.get("bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+    if bound == "hbm":
+        achieved = alg_bytes / ffn_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        achieved = flops / ffn_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4), "traffic": traffic}
+    roof.update({"kernel": FFN_KERNEL, "avg_launch_us": round(ffn_avg_s * 1e6, 2),
+                 "algorithmic_bytes": alg_bytes, "algorithmic_flops": flops,
+                 "bytes_parts": byte_parts,
+                 "mfma_frac": round(flops / ffn_avg_s / 1e12 / peak_flops, 4),
+                 "hbm_frac": round(alg_bytes / ffn_avg_s / 1e9 / PEAK_HBM_GBS, 4)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE FFN TFLOP/s (L1+L2+combine) on 1 MI355X, % of MFMA peak, per schedule",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl.dtype == "fp8" else "bf16",
+        "data": "synthetic (seeded normal inputs, random-init expert weights)",
+        "config": {"workload": wl.name, "schedule": args.schedule, "slices": S,
+                   "tokens_per_slice": T, "experts": wl.num_experts, "top_k": k,
+                   "local_experts": wl.num_local, "hidden": H, "inter": wl.inter,
+                   "routed_rows": R, "sched_rows": P, "max_rows_per_expert": max_rows,
+                   "active_experts": active, "tile": plan.tile, "block_m": plan.block_m,
+                   "block_n": plan.block_n1, "grid": plan.grid, "lead_d": plan.lead_d,
+                   "r_expert": round(max_rows / (wl.num_tokens * k / wl.num_experts), 3)},
+        "pct_of_mfma_peak": round(100 * flops / (ms_per_step * 1e-3) / 1e12 / peak_flops, 2),
+        "ffn_only_ms": round(statistics.mean(ffn_ms), 4),
+        "per_schedule": sched_out,
+        "speedup_interleaved_over_wave": round(speedup, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

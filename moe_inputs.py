@@ -188,24 +188,60 @@ def make_expert_weights(wl: Workload, e: int):
     return f32_to_bf16_bits(w1), None, f32_to_bf16_bits(w2), None
 
 
-def make_inputs(wl: Workload, experts: int | None = None) -> MoeInputs:
+_SHARED = {}
+
+
+def _expert_job(args):
+    """Draw expert e's weights into the arrays of _SHARED (fork workers see
+    the parent's shared mappings, so nothing large is pickled)."""
+    wl, e = args
+    a, a_s, b, b_s = make_expert_weights(wl, e)
+    _SHARED["w1"][e] = a
+    _SHARED["w2"][e] = b
+    if a_s is not None:
+        _SHARED["w1s"][e] = a_s
+        _SHARED["w2s"][e] = b_s
+    return e
+
+
+def _shared_array(shape, dtype):
+    import mmap
+    n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+    buf = mmap.mmap(-1, max(n, 1))   # anonymous MAP_SHARED: visible across fork
+    return np.frombuffer(buf, dtype=dtype, count=int(np.prod(shape))).reshape(shape)
+
+
+def make_inputs(wl: Workload, experts: int | None = None, workers: int = 1) -> MoeInputs:
     """Generate every input of a workload. ``experts`` limits how many local
-    experts' weights are drawn (the rest are left zero) for quick host tests."""
+    experts' weights are drawn (the rest are left zero) for quick host tests.
+    ``workers`` > 1 draws the experts in that many forked processes (each
+    expert has its own seed stream, so the result does not depend on it);
+    call it before the process initialises a GPU."""
     logits, bias = make_logits(wl)
     x, xs = make_x(wl)
     L = wl.num_local
     wdt = np.uint8 if wl.dtype == "fp8" else np.uint16
-    w1 = np.zeros((L, 2 * wl.inter, wl.hidden), dtype=wdt)
-    w2 = np.zeros((L, wl.hidden, wl.inter), dtype=wdt)
+    jobs = [(wl, e) for e in range(L if experts is None else min(experts, L))]
+    parallel = workers > 1 and len(jobs) > 1
+    alloc = _shared_array if parallel else (lambda shape, dt: np.zeros(shape, dt))
+    w1 = alloc((L, 2 * wl.inter, wl.hidden), wdt)
+    w2 = alloc((L, wl.hidden, wl.inter), wdt)
     w1s = w2s = None
     if wl.dtype == "fp8":
-        w1s = np.ones((L, 2 * wl.inter // 128, wl.hidden // 128), dtype=np.float32)
-        w2s = np.ones((L, wl.hidden // 128, wl.inter // 128), dtype=np.float32)
-    for e in range(L if experts is None else min(experts, L)):
-        a, a_s, b, b_s = make_expert_weights(wl, e)
-        w1[e] = a
-        w2[e] = b
-        if w1s is not None:
-            w1s[e] = a_s
-            w2s[e] = b_s
+        w1s = alloc((L, 2 * wl.inter // 128, wl.hidden // 128), np.float32)
+        w2s = alloc((L, wl.hidden // 128, wl.inter // 128), np.float32)
+        w1s[...] = 1.0
+        w2s[...] = 1.0
+    _SHARED.update(w1=w1, w2=w2, w1s=w1s, w2s=w2s)
+    try:
+        if parallel:
+            import concurrent.futures as cf
+            import multiprocessing as mp
+            with cf.ProcessPoolExecutor(min(workers, len(jobs)), mp.get_context("fork")) as ex:
+                list(ex.map(_expert_job, jobs))
+        else:
+            for j in jobs:
+                _expert_job(j)
+    finally:
+        _SHARED.clear()
     return MoeInputs(wl, logits, bias, x, xs, w1, w1s, w2, w2s)

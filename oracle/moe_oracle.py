@@ -217,10 +217,11 @@ def decode_expert(inp, e: int):
     return bf16_bits_to_f64(inp.w1[e]), bf16_bits_to_f64(inp.w2[e])
 
 
-def run(inp, block_m: int = 128, idx=None, w=None) -> OracleResult:
+def run(inp, block_m: int = 128, idx=None, w=None, experts: int | None = None) -> OracleResult:
     """The whole path: routing (unless idx/w are given), layout, per-expert
     FFN over the routed rows of each local expert, weighted combine and the
-    source-side reduction."""
+    source-side reduction. ``experts`` evaluates only the first that many
+    local experts (a bounded sample for timing; other rows stay zero)."""
     wl = inp.wl
     N, k, H = wl.num_tokens, wl.top_k, wl.hidden
     if idx is None:
@@ -228,7 +229,7 @@ def run(inp, block_m: int = 128, idx=None, w=None) -> OracleResult:
     lay = dispatch_layout(idx, wl.local_begin, wl.num_local, block_m)
     x = decode_x(inp)
     Y = np.zeros((lay.total_rows, H), dtype=np.float64)
-    for e in range(wl.num_local):
+    for e in range(wl.num_local if experts is None else min(experts, wl.num_local)):
         r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
         if r1 == r0:
             continue
