@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "internal.hpp"
@@ -144,11 +145,17 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     if (!t) return MOE_ERR_INVALID_ARG;
     if (!tile_fits(t, s)) return MOE_ERR_UNSUPPORTED;
   } else {
-    // expected rows per local expert under uniform routing
+    // expected rows per local expert under uniform routing; pick the
+    // smallest M-block that holds a typical expert whole (so each weight
+    // tile is streamed once), the large block when experts are big
     const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
-    const int order_small[] = {3, 1, 2};
-    const int order_large[] = {1, 2, 3};
-    const int* order = avg <= 48.0 ? order_small : order_large;
+    const double hi = avg + 4.0 * std::sqrt(avg);
+    int order[3] = {1, 2, 3};
+    if (avg <= 24.0) {
+      order[0] = 3; order[1] = 2; order[2] = 1;
+    } else if (hi <= 192.0) {
+      order[0] = 2; order[1] = 1; order[2] = 3;
+    }
     for (int i = 0; i < 3 && !t; ++i)
       if (tile_fits(find_tile(order[i]), s)) t = find_tile(order[i]);
     if (!t) return MOE_ERR_UNSUPPORTED;

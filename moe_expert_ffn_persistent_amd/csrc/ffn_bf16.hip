@@ -38,28 +38,34 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int TM_, int TN_, int WT_, int WF_>
+template <int TM_, int TN_, int WT_, int WF_, int BK_, int NS_>
 struct Cfg {
   static constexpr int TM = TM_;          // tokens per M-block (b_m)
   static constexpr int TN = TN_;          // features per N-tile (b_n)
   static constexpr int WT = WT_;          // wavefronts along tokens
   static constexpr int WF = WF_;          // wavefronts along features
-  static constexpr int BK = 64;           // K elements per stage
-  static constexpr int THREADS = 64 * WT * WF;
+  static constexpr int BK = BK_;          // K elements per stage
+  static constexpr int NS = NS_;          // LDS ring stages
+  static constexpr int NW = WT * WF;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int TT = TM / WT;      // tokens per wavefront
   static constexpr int FT = TN / WF;      // features per wavefront
   static constexpr int TB = TT / 32;      // 32-token MFMA blocks per wavefront
   static constexpr int FB = FT / 32;      // 32-feature MFMA blocks per wavefront
   static constexpr int ROW_BYTES = BK * 2;
-  static constexpr int CPR = ROW_BYTES / 16;           // 16-byte chunks per row
-  static constexpr int RPP = THREADS / CPR;            // rows per copy pass
-  static constexpr int LW = TN / RPP;                  // weight rows per thread
-  static constexpr int LT = TM / RPP;                  // token rows per thread
+  static constexpr int CPR = ROW_BYTES / 16;      // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;            // rows per 1 KiB DMA instruction
+  static constexpr int SWZ_SHIFT = CPR == 8 ? 0 : 1;
+  static constexpr int SWZ_MASK = CPR - 1;
+  static constexpr int NI = (TN + TM) / RPI / NW; // DMA instructions per wavefront per stage
   static constexpr int A_BYTES = TN * ROW_BYTES;
   static constexpr int STAGE_BYTES = (TN + TM) * ROW_BYTES;
   static_assert(TT % 32 == 0 && FT % 32 == 0, "wavefront tile must be a multiple of 32");
   static_assert(FB % 2 == 0, "gate/up pairing needs an even number of feature blocks");
-  static_assert(TN % RPP == 0 && TM % RPP == 0, "copy passes must tile the block");
+  static_assert(CPR == 8 || CPR == 4, "rows of 64 or 128 bytes");
+  static_assert(TN % RPI == 0 && TM % RPI == 0, "DMA instructions must not straddle operands");
+  static_assert(((TN + TM) / RPI) % NW == 0, "DMA instructions must split evenly over wavefronts");
+  static_assert(NS >= 2 && NI * (NS - 2) <= 63, "vmcnt range");
 };
 
 struct Meta {
@@ -80,34 +86,63 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
 
+// One 1 KiB global->LDS copy for the wavefront: lane l's 16 bytes from src
+// land at LDS byte address m0 + 16*l. Issued from inline assembly so the
+// compiler does not serialise later LDS reads behind it; completion is
+// awaited explicitly with vm_wait and published with lds_barrier.
+__device__ __forceinline__ void dma16(const char* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most NI*ahead of this wavefront's copies are outstanding
+template <int NI, int K>
+__device__ __forceinline__ void vm_wait_ahead(int ahead) {
+  if constexpr (K == 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= K) vm_wait<NI * K>();
+    else vm_wait_ahead<NI, K - 1>(ahead);
+  }
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <class C>
 struct Tile {
-  const char* pa[C::LW];   // weight row bases (bytes)
-  const char* pb[C::LT];   // token row bases (bytes)
-  uint4 ra[C::LW];
-  uint4 rb[C::LT];
+  const char* src[C::NI];   // this lane's copy sources for stage 0
   f32x16 acc[C::FB][C::TB];
+  uint32_t ring;            // LDS byte address of the ring
 
-  __device__ __forceinline__ void load(int kt) {
-    const int col = (threadIdx.x % C::CPR) * 16 + kt * C::ROW_BYTES;
+  // Copy sources: instruction i of wavefront w fills LDS rows
+  // [j*RPI, (j+1)*RPI) of a stage, j = w + NW*i; lane l takes row
+  // j*RPI + l/CPR and the logical chunk that lands at its physical slot.
+  template <class WRow, class TRow>
+  __device__ __forceinline__ void setup(WRow wrow, TRow trow) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < C::LW; ++i) ra[i] = *reinterpret_cast<const uint4*>(pa[i] + col);
-#pragma unroll
-    for (int i = 0; i < C::LT; ++i) rb[i] = *reinterpret_cast<const uint4*>(pb[i] + col);
+    for (int i = 0; i < C::NI; ++i) {
+      const int j = wave + C::NW * i;
+      const int r = j * C::RPI + lane / C::CPR;
+      const int c = (lane % C::CPR) ^ ((r >> C::SWZ_SHIFT) & C::SWZ_MASK);
+      const char* base = j * C::RPI < C::TN ? wrow(r) : trow(r - C::TN);
+      src[i] = base + c * 16;
+    }
   }
 
-  __device__ __forceinline__ void store(char* stage) {
-    const int c = threadIdx.x % C::CPR;
-    const int r0 = threadIdx.x / C::CPR;
+  __device__ __forceinline__ void issue(int kt, int slot) {
+    const int wave = threadIdx.x >> 6;
+    const size_t off = (size_t)kt * C::ROW_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::LW; ++i) {
-      const int r = r0 + i * C::RPP;
-      *reinterpret_cast<uint4*>(stage + r * C::ROW_BYTES + ((c ^ (r & 7)) << 4)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::LT; ++i) {
-      const int r = r0 + i * C::RPP;
-      *reinterpret_cast<uint4*>(stage + C::A_BYTES + r * C::ROW_BYTES + ((c ^ (r & 7)) << 4)) = rb[i];
+    for (int i = 0; i < C::NI; ++i) {
+      const int j = wave + C::NW * i;
+      dma16(src[i] + off, uni(ring + slot * C::STAGE_BYTES + j * 1024));
     }
   }
 
@@ -115,9 +150,10 @@ struct Tile {
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
     const int half = lane >> 5;
+    const int swz = (r_lane >> C::SWZ_SHIFT) & C::SWZ_MASK;
 #pragma unroll
     for (int ks = 0; ks < C::BK / 16; ++ks) {
-      const int chunk = ((2 * ks + half) ^ (lane & 7)) << 4;
+      const int chunk = ((2 * ks + half) ^ swz) << 4;
       bf16x8 af[C::FB], bf[C::TB];
 #pragma unroll
       for (int fb = 0; fb < C::FB; ++fb) {
@@ -138,27 +174,33 @@ struct Tile {
     }
   }
 
-  // Full K loop over nk stages of BK; acc starts at zero.
+  // Full K loop over nk stages of BK through an NS-stage LDS ring: stage kt
+  // is awaited (own copies, then the workgroup barrier), the copy of stage
+  // kt+NS-1 is issued into the slot stage kt-1 used, then stage kt is
+  // multiplied. acc starts at zero.
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) acc[fb][tb] = f32x16{};
-    load(0);
-    store(lds);
-    __syncthreads();
+    lds_barrier();   // every wavefront is done reading the ring of the previous tile
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s)
+      if (s < nk) issue(s, s);
+    int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(kt + 1);
-      compute(lds + (kt & 1) * C::STAGE_BYTES, wf, wt);
-      if (kt + 1 < nk) store(lds + ((kt + 1) & 1) * C::STAGE_BYTES);
-      __syncthreads();
+      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+      lds_barrier();
+      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1);
+      compute(lds + slot * C::STAGE_BYTES, wf, wt);
+      slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
   }
 };
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
   __shared__ Meta meta;
 
   const int tid = threadIdx.x;
@@ -181,21 +223,27 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     meta.nwaves = build_waves(meta.tile_off, L, a.N1, a.grid, a.experts_per_wave, meta.wave_row);
   __syncthreads();
   const int P = uni(meta.tile_off[L]);
+  // logical instance id: workgroups are dispatched round-robin over the 8
+  // XCDs, so consecutive logical ids are placed on the same XCD (and share
+  // its L2) when the grid is a multiple of 8
+  const int G = a.grid;
+  const int g = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
 
   InterleavedStream ist;
   ExpertWaveStream ews;
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
-  if (interleaved) ist.init(blockIdx.x, a.grid, P, a.N1, a.N2, a.lead_d);
-  else ews.init(blockIdx.x, a.grid, a.N1, a.N2, meta.wave_row, uni(meta.nwaves));
+  if (interleaved) ist.init(g, G, P, a.N1, a.N2, a.lead_d);
+  else ews.init(g, G, a.N1, a.N2, meta.wave_row, uni(meta.nwaves));
 
   Tile<C> tile;
+  tile.ring = (uint32_t)(uintptr_t)lds;
   int seq = 0;
   for (;;) {
     const Task t = interleaved ? ist.next() : ews.next();
     if (t.kind == 0) break;
     const int p = uni(t.p), n = uni(t.n);
     if (a.trace && tid == 0 && seq < a.trace_cap) {
-      uint32_t* rec = a.trace + ((size_t)blockIdx.x * a.trace_cap + seq) * 2;
+      uint32_t* rec = a.trace + ((size_t)g * a.trace_cap + seq) * 2;
       rec[0] = (uint32_t)t.kind | ((uint32_t)n << 2);
       rec[1] = (uint32_t)p;
     }
@@ -204,29 +252,25 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     const int m = p - uni(meta.tile_off[e]);
     const int r_base = uni(meta.row_off[e]);
     const int Me = uni(meta.row_off[e + 1]) - r_base;
-    const int r0 = tid / C::CPR;
 
     if (t.kind == 1) {
       if (p == a.debug_skip_row) continue;
       // ---- Linear-1: gate/up rows of W1[e], gathered token rows of x ----
       const char* w1e = static_cast<const char*>(a.w1) + (size_t)e * 2 * I * H * 2;
       const int j0 = n * (C::TN / 2);
-#pragma unroll
-      for (int i = 0; i < C::LW; ++i) {
-        const int q = r0 + i * C::RPP;
-        const int blk = q >> 5;
-        const int wrow = ((blk & 1) ? I : 0) + j0 + (blk >> 1) * 32 + (q & 31);
-        tile.pa[i] = w1e + (size_t)wrow * H * 2;
-      }
-#pragma unroll
-      for (int i = 0; i < C::LT; ++i) {
-        const int q = r0 + i * C::RPP;
-        const int mm = min(m * C::TM + q, Me - 1);
-        const int f = a.row_pair[r_base + mm];
-        const int tok = f / K;
-        const int s = tok / T;
-        tile.pb[i] = meta.x[s] + (size_t)(tok - s * T) * H * 2;
-      }
+      tile.setup(
+          [&](int q) {   // tile row q: 32-row blocks alternate gate and up rows
+            const int blk = q >> 5;
+            const int wrow = ((blk & 1) ? I : 0) + j0 + (blk >> 1) * 32 + (q & 31);
+            return w1e + (size_t)wrow * H * 2;
+          },
+          [&](int q) {   // gathered token row; padding rows repeat the last routed row
+            const int mm = min(m * C::TM + q, Me - 1);
+            const int f = a.row_pair[r_base + mm];
+            const int tok = f / K;
+            const int s = tok / T;
+            return meta.x[s] + (size_t)(tok - s * T) * H * 2;
+          });
       tile.mainloop(lds, H / C::BK, wf, wt);
       // SwiGLU epilogue: h[p*TM + token][j0 + column] in bf16
       char* hb = static_cast<char*>(a.h);
@@ -277,16 +321,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       // ---- Linear-2: rows of W2[e], rows of h ----
       const char* w2e = static_cast<const char*>(a.w2) + (size_t)e * H * I * 2;
       const char* hb = static_cast<const char*>(a.h);
-#pragma unroll
-      for (int i = 0; i < C::LW; ++i) {
-        const int q = r0 + i * C::RPP;
-        tile.pa[i] = w2e + (size_t)(n * C::TN + q) * I * 2;
-      }
-#pragma unroll
-      for (int i = 0; i < C::LT; ++i) {
-        const int q = r0 + i * C::RPP;
-        tile.pb[i] = hb + ((size_t)p * C::TM + q) * I * 2;
-      }
+      tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; },
+                 [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
       tile.mainloop(lds, I / C::BK, wf, wt);
       // weighted combine stores
 #pragma unroll
@@ -331,9 +367,10 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 }
 
 // Tile configurations (ids are part of the plan, stable within a build).
-using CfgLarge = Cfg<256, 256, 2, 2>;   // 128x128 per wavefront, prefill-sized experts
-using CfgMid = Cfg<128, 256, 2, 2>;     // 128 features x 64 tokens per wavefront
-using CfgSmall = Cfg<32, 128, 1, 2>;    // decode-sized experts: 64 features x 32 tokens
+// Cfg<tokens, features, token waves, feature waves, BK, ring stages>
+using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill-sized experts
+using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
+using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
