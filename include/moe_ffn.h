@@ -107,9 +107,16 @@ typedef struct {
   int32_t timeout_ms;        /* dependency-wait limit; 0 = 2000 ms                         */
   int32_t* status;           /* device int32, or NULL: set to MOE_ERR_TIMEOUT by a wait
                                 that gave up (never cleared by the library)                */
-  uint32_t* trace;           /* device [grid][trace_capacity][2] task records, or NULL:
+  uint32_t* trace;           /* device [grid][trace_capacity][8] task records of each
+                                persistent workgroup, in execution order, or NULL:
                                 word 0 = kind (1 = Linear-1, 2 = Linear-2) | n << 2,
-                                word 1 = scheduler row p; unused records stay untouched    */
+                                word 1 = scheduler row p,
+                                words 2..5 = low 32 bits of the device wall clock
+                                (moe_plan.wall_clock_khz) at task start, after the
+                                dependency wait, after the mainloop, after the
+                                epilogue's stores were issued (Linear-2) or the row
+                                counter was published (Linear-1); words 6..7 = 0.
+                                Unused records stay untouched                          */
   int32_t trace_capacity;    /* records per workgroup                                      */
   int32_t debug_skip_l1_row; /* testing only: when >= 0, Linear-1 tiles of this scheduler
                                 row are not run, so its Linear-2 waits time out            */
@@ -127,6 +134,7 @@ typedef struct {
   int32_t lead_d;      /* resolved D                                    */
   int32_t max_sched_rows;    /* upper bound of P for this shape          */
   size_t workspace_bytes;    /* bytes moe_ffn_forward needs              */
+  int32_t wall_clock_khz;    /* frequency of the trace time stamps       */
 } moe_plan;
 
 /* Library version (MOE_FFN_ABI_VERSION). */

@@ -51,7 +51,10 @@ class MoeSchedParams(ctypes.Structure):
 class MoePlan(ctypes.Structure):
     _fields_ = [("tile", c_i32), ("block_m", c_i32), ("block_n1", c_i32), ("block_n2", c_i32),
                 ("n1_tiles", c_i32), ("n2_tiles", c_i32), ("grid", c_i32), ("lead_d", c_i32),
-                ("max_sched_rows", c_i32), ("workspace_bytes", ctypes.c_size_t)]
+                ("max_sched_rows", c_i32), ("workspace_bytes", ctypes.c_size_t),
+                ("wall_clock_khz", c_i32)]
+
+TRACE_WORDS = 8
 
 
 class MoeError(RuntimeError):

@@ -16,7 +16,7 @@ hipError_t occupancy_ffn_bf16(int id, int* n);
 
 namespace {
 
-constexpr int kNumBf16Tiles = 3;
+constexpr int kNumBf16Tiles = 5;
 
 struct DeviceProps {
   bool ready = false;
@@ -149,14 +149,16 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     // smallest M-block that holds a typical expert whole (so each weight
     // tile is streamed once), the large block when experts are big
     const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
-    const double hi = avg + 4.0 * std::sqrt(avg);
-    int order[3] = {1, 2, 3};
+    const double sd = std::sqrt(avg);
+    int order[5] = {1, 2, 5, 3, 4};
     if (avg <= 24.0) {
-      order[0] = 3; order[1] = 2; order[2] = 1;
-    } else if (hi <= 192.0) {
-      order[0] = 2; order[1] = 1; order[2] = 3;
+      order[0] = 3; order[1] = 5; order[2] = 2; order[3] = 1;
+    } else if (avg + 2.5 * sd <= 160.0) {
+      order[0] = 5; order[1] = 2; order[2] = 1; order[3] = 3;
+    } else if (avg + 4.0 * sd <= 192.0) {
+      order[0] = 2; order[1] = 5; order[2] = 1; order[3] = 3;
     }
-    for (int i = 0; i < 3 && !t; ++i)
+    for (int i = 0; i < 5 && !t; ++i)
       if (tile_fits(find_tile(order[i]), s)) t = find_tile(order[i]);
     if (!t) return MOE_ERR_UNSUPPORTED;
   }
@@ -181,6 +183,7 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
   long long rows = (pairs + (long long)s->num_local_experts * (t->block_m - 1)) / t->block_m;
   p.max_sched_rows = (int)std::max<long long>(rows, 1);
   p.workspace_bytes = carve(s, p.block_m, p.max_sched_rows).total;
+  p.wall_clock_khz = dp->wall_khz;
   *out = p;
   return MOE_OK;
 }

@@ -24,9 +24,15 @@
 //    current stage's MFMAs and written to the other stage after them.
 //  - Linear-1 N-tiles interleave gate and up rows in 32-row blocks, so the
 //    gate and up accumulators of one output column sit in the same lane.
-//  - h and l2_full cross XCDs (each XCD has its own L2): the producer
-//    releases at agent scope (L2 write-back) before the counter increment,
-//    the consumer acquires at agent scope (L2 invalidate) before reading h.
+//  - h and l2_full cross XCDs (each XCD has its own L2): the producer writes
+//    h with device-scope (sc1) stores that go through its L2, waits for them
+//    to complete, then bumps the counter with a device-scope atomic; the
+//    consumer polls the counter with device-scope loads and copies h with
+//    device-scope (sc1) loads, which are never served from a stale L2 line.
+//    No whole-L2 write-back or invalidate is needed on either side.
+//  - Every N-tile of a row re-reads the row's x (or h) tile, so wide N-tiles
+//    (512 features) are used where registers allow: they halve that re-read
+//    traffic, which otherwise competes with the weight stream for L2.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -70,7 +76,6 @@ struct Cfg {
 
 struct Meta {
   int tile_off[MOE_MAX_LOCAL_EXPERTS + 1];
-  int row_off[MOE_MAX_LOCAL_EXPERTS + 1];
   int wave_row[MOE_MAX_LOCAL_EXPERTS + 2];
   const char* x[MOE_MAX_SLICES];
   char* comb[MOE_MAX_SLICES];
@@ -90,9 +95,30 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); 
 // land at LDS byte address m0 + 16*l. Issued from inline assembly so the
 // compiler does not serialise later LDS reads behind it; completion is
 // awaited explicitly with vm_wait and published with lds_barrier.
+// Cache policy of a copy: kCacheNormal (weights and x rows; measured on
+// MI355X, non-temporal copies stream weights markedly slower), kStream (nt),
+// kCoherent (sc1, device scope: never served from a possibly stale L2 line of
+// this XCD) for h, which other XCDs produced during this launch.
+enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
+
+#ifndef MOE_WEIGHT_POLICY
+#define MOE_WEIGHT_POLICY kCacheNormal
+#endif
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+
+template <int POL>
 __device__ __forceinline__ void dma16(const char* src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
-               : "memory", "m0");
+  if constexpr (POL == kStream)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  else if constexpr (POL == kCoherent)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
 }
 
 template <int N>
@@ -136,13 +162,19 @@ struct Tile {
     }
   }
 
-  __device__ __forceinline__ void issue(int kt, int slot) {
+  // WPOL / TPOL: cache policy of the weight / token rows
+  // weight rows use MOE_WEIGHT_POLICY; token rows are copied with
+  // device-scope loads when `coherent` (h written during this launch)
+  __device__ __forceinline__ void issue(int kt, int slot, bool coherent) {
     const int wave = threadIdx.x >> 6;
     const size_t off = (size_t)kt * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
       const int j = wave + C::NW * i;
-      dma16(src[i] + off, uni(ring + slot * C::STAGE_BYTES + j * 1024));
+      const uint32_t dst = uni(ring + slot * C::STAGE_BYTES + j * 1024);
+      if (j * C::RPI < C::TN) dma16<MOE_WEIGHT_POLICY>(src[i] + off, dst);
+      else if (coherent) dma16<kCoherent>(src[i] + off, dst);
+      else dma16<kCacheNormal>(src[i] + off, dst);
     }
   }
 
@@ -178,7 +210,7 @@ struct Tile {
   // is awaited (own copies, then the workgroup barrier), the copy of stage
   // kt+NS-1 is issued into the slot stage kt-1 used, then stage kt is
   // multiplied. acc starts at zero.
-  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
+  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, bool coherent) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
@@ -186,12 +218,12 @@ struct Tile {
     lds_barrier();   // every wavefront is done reading the ring of the previous tile
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
-      if (s < nk) issue(s, s);
+      if (s < nk) issue(s, s, coherent);
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
       vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
       lds_barrier();
-      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1);
+      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
       compute(lds + slot * C::STAGE_BYTES, wf, wt);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
@@ -210,10 +242,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   const int wt = wave / C::WF;
   const int L = a.L, H = a.H, I = a.I, K = a.k, T = a.T;
 
-  for (int i = tid; i <= L; i += C::THREADS) {
-    meta.tile_off[i] = a.tile_offset[i];
-    meta.row_off[i] = a.row_offset[i];
-  }
+  for (int i = tid; i <= L; i += C::THREADS) meta.tile_off[i] = a.tile_offset[i];
   for (int i = tid; i < a.S; i += C::THREADS) {
     meta.x[i] = static_cast<const char*>(a.x[i]);
     meta.comb[i] = static_cast<char*>(a.comb[i]);
@@ -242,60 +271,26 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     const Task t = interleaved ? ist.next() : ews.next();
     if (t.kind == 0) break;
     const int p = uni(t.p), n = uni(t.n);
-    if (a.trace && tid == 0 && seq < a.trace_cap) {
-      uint32_t* rec = a.trace + ((size_t)g * a.trace_cap + seq) * 2;
+    // task record (thread 0 only): kind | n << 2, p, then wall-clock stamps
+    uint32_t* rec = (a.trace && tid == 0 && seq < a.trace_cap)
+                        ? a.trace + ((size_t)g * a.trace_cap + seq) * kTraceWords
+                        : nullptr;
+    if (rec) {
       rec[0] = (uint32_t)t.kind | ((uint32_t)n << 2);
       rec[1] = (uint32_t)p;
+      rec[2] = (uint32_t)wall_clock64();
+      rec[6] = 0u;
+      rec[7] = 0u;
     }
     ++seq;
     const int e = expert_of_row(meta.tile_off, L, p);
     const int m = p - uni(meta.tile_off[e]);
-    const int r_base = uni(meta.row_off[e]);
-    const int Me = uni(meta.row_off[e + 1]) - r_base;
+    const int r_base = uni(a.row_offset[e]);
+    const int Me = uni(a.row_offset[e + 1]) - r_base;
 
-    if (t.kind == 1) {
+    const bool l1 = t.kind == 1;
+    if (l1) {
       if (p == a.debug_skip_row) continue;
-      // ---- Linear-1: gate/up rows of W1[e], gathered token rows of x ----
-      const char* w1e = static_cast<const char*>(a.w1) + (size_t)e * 2 * I * H * 2;
-      const int j0 = n * (C::TN / 2);
-      tile.setup(
-          [&](int q) {   // tile row q: 32-row blocks alternate gate and up rows
-            const int blk = q >> 5;
-            const int wrow = ((blk & 1) ? I : 0) + j0 + (blk >> 1) * 32 + (q & 31);
-            return w1e + (size_t)wrow * H * 2;
-          },
-          [&](int q) {   // gathered token row; padding rows repeat the last routed row
-            const int mm = min(m * C::TM + q, Me - 1);
-            const int f = a.row_pair[r_base + mm];
-            const int tok = f / K;
-            const int s = tok / T;
-            return meta.x[s] + (size_t)(tok - s * T) * H * 2;
-          });
-      tile.mainloop(lds, H / C::BK, wf, wt);
-      // SwiGLU epilogue: h[p*TM + token][j0 + column] in bf16
-      char* hb = static_cast<char*>(a.h);
-#pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
-        char* hrow = hb + ((size_t)p * C::TM + tok_l) * I * 2;
-#pragma unroll
-        for (int fp = 0; fp < C::FB / 2; ++fp) {
-          const int col0 = j0 + (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            float hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              hv[i] = silu(tile.acc[2 * fp][tb][g4 * 4 + i]) * tile.acc[2 * fp + 1][tb][g4 * 4 + i];
-            uint2 v = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            *reinterpret_cast<uint2*>(hrow + (size_t)(col0 + g4 * 8) * 2) = v;
-          }
-        }
-      }
-      // publish: h visible at agent scope, then count the tile for row p
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // ---- wait until every Linear-1 tile of row p has published h ----
       if (tid == 0) {
@@ -317,13 +312,71 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       const int ok = uni(meta.flag);
       __syncthreads();
       if (!ok) continue;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      // ---- Linear-2: rows of W2[e], rows of h ----
+      // h is read with device-scope (sc1) copies, which never hit a stale
+      // line of this XCD's L2, so no L2 invalidate is needed here
+    }
+    if (rec) rec[3] = (uint32_t)wall_clock64();
+
+    // ---- operands of the task: one mainloop serves both GEMMs ----
+    const int j0 = n * (C::TN / 2);   // Linear-1: first intermediate column
+    if (l1) {
+      // gate/up rows of W1[e] (32-row blocks alternate gate and up rows) and
+      // the gathered token rows of x; padding rows repeat the last routed row
+      const char* w1e = static_cast<const char*>(a.w1) + (size_t)e * 2 * I * H * 2;
+      tile.setup(
+          [&](int q) {
+            const int blk = q >> 5;
+            const int wrow = ((blk & 1) ? I : 0) + j0 + (blk >> 1) * 32 + (q & 31);
+            return w1e + (size_t)wrow * H * 2;
+          },
+          [&](int q) {
+            const int mm = min(m * C::TM + q, Me - 1);
+            const int f = a.row_pair[r_base + mm];
+            const int tok = f / K;
+            const int s = tok / T;
+            return meta.x[s] + (size_t)(tok - s * T) * H * 2;
+          });
+    } else {
+      // rows of W2[e] and the block's rows of h
       const char* w2e = static_cast<const char*>(a.w2) + (size_t)e * H * I * 2;
       const char* hb = static_cast<const char*>(a.h);
       tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; },
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
-      tile.mainloop(lds, I / C::BK, wf, wt);
+    }
+    tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, !l1);
+    if (rec) rec[4] = (uint32_t)wall_clock64();
+
+    if (l1) {
+      // SwiGLU epilogue: h[p*TM + token][j0 + column] in bf16
+      char* hb = static_cast<char*>(a.h);
+#pragma unroll
+      for (int tb = 0; tb < C::TB; ++tb) {
+        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
+        char* hrow = hb + ((size_t)p * C::TM + tok_l) * I * 2;
+#pragma unroll
+        for (int fp = 0; fp < C::FB / 2; ++fp) {
+          const int col0 = j0 + (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              hv[i] = silu(tile.acc[2 * fp][tb][g4 * 4 + i]) * tile.acc[2 * fp + 1][tb][g4 * 4 + i];
+            const uint64_t v = (uint64_t)pack_bf16x2(hv[0], hv[1]) |
+                               ((uint64_t)pack_bf16x2(hv[2], hv[3]) << 32);
+            // device-scope store: written through this XCD's L2
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(hrow + (size_t)(col0 + g4 * 8) * 2), v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+      // publish: every wavefront's device-scope h stores have completed
+      // (vmcnt drained) before the row counter moves
+      vm_wait<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (rec) rec[5] = (uint32_t)wall_clock64();
+    } else {
       // weighted combine stores
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
@@ -342,12 +395,18 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               const f32x16& v = tile.acc[fb][tb];
-              uint2 o = {pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]),
-                         pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3])};
-              *reinterpret_cast<uint2*>(dst + (size_t)(col0 + g4 * 8) * 2) = o;
+              const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
+                                 ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
+              uint64_t* d = reinterpret_cast<uint64_t*>(dst + (size_t)(col0 + g4 * 8) * 2);
+              if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);   // not re-read by this kernel
+              else *d = o;
             }
           }
         }
+      }
+      if (rec) {
+        vm_wait<0>();   // the stamp covers the issue of this wavefront's stores
+        rec[5] = (uint32_t)wall_clock64();
       }
     }
   }
@@ -371,6 +430,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill-sized experts
 using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
 using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
+using CfgWide = Cfg<192, 512, 2, 2, 32, 3>;    // 256x96: as Mid, half the x/h re-reads
+using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -390,6 +451,8 @@ const TileInfo kBf16Tiles[] = {
     {1, MOE_BF16, CfgLarge::TM, CfgLarge::TN, CfgLarge::THREADS},
     {2, MOE_BF16, CfgMid::TM, CfgMid::TN, CfgMid::THREADS},
     {3, MOE_BF16, CfgSmall::TM, CfgSmall::TN, CfgSmall::THREADS},
+    {4, MOE_BF16, CfgWide::TM, CfgWide::TN, CfgWide::THREADS},
+    {5, MOE_BF16, CfgMid64::TM, CfgMid64::TN, CfgMid64::THREADS},
 };
 
 hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
@@ -397,6 +460,8 @@ hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
     case 1: return launch<CfgLarge>(a, s);
     case 2: return launch<CfgMid>(a, s);
     case 3: return launch<CfgSmall>(a, s);
+    case 4: return launch<CfgWide>(a, s);
+    case 5: return launch<CfgMid64>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -406,6 +471,8 @@ hipError_t occupancy_ffn_bf16(int id, int* n) {
     case 1: return occupancy<CfgLarge>(n);
     case 2: return occupancy<CfgMid>(n);
     case 3: return occupancy<CfgSmall>(n);
+    case 4: return occupancy<CfgWide>(n);
+    case 5: return occupancy<CfgMid64>(n);
   }
   return hipErrorInvalidValue;
 }

@@ -114,7 +114,7 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
     ref = mo.run(inp, block_m=32)
     up = Uploaded(inp)
     cap = 4096
-    trace = torch.full((grid, cap, 2), -1, dtype=torch.int32, device=dev())
+    trace = torch.full((grid, cap, 8), -1, dtype=torch.int32, device=dev())
     ffn = make_ffn(wl, tile=3)
     print(f"[ffn] trace {schedule} grid={grid} D={lead} epw={epw}", flush=True)
     _route_and_layout(ffn, up)
@@ -132,6 +132,9 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
         used = recs[recs[:, 0] != -1]
         got = [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used]
         assert got == want[g], f"instance {g}"
+        # stamps are ordered within each record: start <= ready <= mainloop end <= done
+        st = used[:, 2:6].astype(np.int64) & 0xFFFFFFFF
+        assert (np.diff(st, axis=1) >= 0).all() or (st.max() - st.min() > 2 ** 31)
 
 
 def test_watchdog_reports_timeout_instead_of_hanging():
@@ -215,4 +218,30 @@ def test_all_tokens_on_one_expert_many_blocks():
             up.reset_combine()
             run_forward(ffn, up, schedule=sched)
             torch.cuda.synchronize()
+            _check_against_oracle(up, ref)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_h_handoff_across_calls_with_poisoned_workspace(tile):
+    # h crosses XCDs inside one launch; poisoning the h region between calls
+    # (and changing the inputs) makes any read of a stale or unwritten h line
+    # visible as a wrong or non-finite output
+    wl = _small_wl(hidden=1024, inter=512, tokens_per_slice=96, num_local=8, num_experts=24,
+                   top_k=4, seed=901)
+    wl2 = _small_wl(hidden=1024, inter=512, tokens_per_slice=96, num_local=8, num_experts=24,
+                    top_k=4, seed=902)
+    ffn = make_ffn(wl, tile=tile)
+    h_bytes = ffn.plan.max_sched_rows * ffn.plan.block_m * wl.inter * 2
+    for w_ in (wl, wl2, wl):
+        inp = mi.make_inputs(w_)
+        ref = mo.run(inp, block_m=16)
+        up = Uploaded(inp)
+        _route_and_layout(ffn, up)
+        for sched in ("expert_wave", "interleaved"):
+            ffn.workspace[:h_bytes].fill_(0xFF)
+            up.reset_combine()
+            print(f"[ffn] poisoned-h tile={tile} seed={w_.seed} {sched}", flush=True)
+            run_forward(ffn, up, schedule=sched)
+            torch.cuda.synchronize()
+            assert int(ffn.status.item()) == 0
             _check_against_oracle(up, ref)
