@@ -11,12 +11,12 @@
 namespace moe {
 
 extern const TileInfo kBf16Tiles[];
+extern const int kNumBf16Tiles;
 hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s);
 hipError_t occupancy_ffn_bf16(int id, int* n);
 
 namespace {
 
-constexpr int kNumBf16Tiles = 5;
 
 struct DeviceProps {
   bool ready = false;
@@ -39,8 +39,9 @@ int device_props(DeviceProps** out) {
     if (hipDeviceGetAttribute(&p.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
         p.wall_khz <= 0)
       p.wall_khz = 100000;
-    for (int id = 1; id <= kNumBf16Tiles; ++id) {
+    for (int i = 0; i < kNumBf16Tiles; ++i) {
       int n = 0;
+      const int id = kBf16Tiles[i].id;
       if (occupancy_ffn_bf16(id, &n) != hipSuccess) return MOE_ERR_HIP;
       p.occ[id] = n;
     }
@@ -150,7 +151,7 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     // tile is streamed once), the large block when experts are big
     const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
     const double sd = std::sqrt(avg);
-    int order[5] = {1, 2, 5, 3, 4};
+    int order[4] = {1, 2, 5, 3};
     if (avg <= 24.0) {
       order[0] = 3; order[1] = 5; order[2] = 2; order[3] = 1;
     } else if (avg + 2.5 * sd <= 160.0) {
@@ -158,7 +159,7 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     } else if (avg + 4.0 * sd <= 192.0) {
       order[0] = 2; order[1] = 5; order[2] = 1; order[3] = 3;
     }
-    for (int i = 0; i < 5 && !t; ++i)
+    for (int i = 0; i < 4 && !t; ++i)
       if (tile_fits(find_tile(order[i]), s)) t = find_tile(order[i]);
     if (!t) return MOE_ERR_UNSUPPORTED;
   }

@@ -30,9 +30,10 @@
 //    consumer polls the counter with device-scope loads and copies h with
 //    device-scope (sc1) loads, which are never served from a stale L2 line.
 //    No whole-L2 write-back or invalidate is needed on either side.
-//  - Every N-tile of a row re-reads the row's x (or h) tile, so wide N-tiles
-//    (512 features) are used where registers allow: they halve that re-read
-//    traffic, which otherwise competes with the weight stream for L2.
+//  - Copies move whole 128-byte row segments where the LDS budget allows
+//    (BK = 64): measured on MI355X, 64-byte segments and the gathered token
+//    rows that every N-tile of a row re-reads limit the weight stream long
+//    before HBM does.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -106,6 +107,9 @@ enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
 #endif
 #ifndef MOE_COMBINE_NT
 #define MOE_COMBINE_NT 1
+#endif
+#ifndef MOE_H_COHERENT
+#define MOE_H_COHERENT 1
 #endif
 
 template <int POL>
@@ -241,6 +245,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   const int wf = wave % C::WF;
   const int wt = wave / C::WF;
   const int L = a.L, H = a.H, I = a.I, K = a.k, T = a.T;
+  if (!MOE_H_COHERENT) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   for (int i = tid; i <= L; i += C::THREADS) meta.tile_off[i] = a.tile_offset[i];
   for (int i = tid; i < a.S; i += C::THREADS) {
@@ -343,7 +348,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; },
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
     }
-    tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, !l1);
+    tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, MOE_H_COHERENT && !l1);
     if (rec) rec[4] = (uint32_t)wall_clock64();
 
     if (l1) {
@@ -430,7 +435,6 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill-sized experts
 using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
 using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
-using CfgWide = Cfg<192, 512, 2, 2, 32, 3>;    // 256x96: as Mid, half the x/h re-reads
 using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
 
 template <class C>
@@ -447,20 +451,20 @@ hipError_t occupancy(int* n) {
 }  // namespace
 
 extern const TileInfo kBf16Tiles[];
+extern const int kNumBf16Tiles;
 const TileInfo kBf16Tiles[] = {
     {1, MOE_BF16, CfgLarge::TM, CfgLarge::TN, CfgLarge::THREADS},
     {2, MOE_BF16, CfgMid::TM, CfgMid::TN, CfgMid::THREADS},
     {3, MOE_BF16, CfgSmall::TM, CfgSmall::TN, CfgSmall::THREADS},
-    {4, MOE_BF16, CfgWide::TM, CfgWide::TN, CfgWide::THREADS},
     {5, MOE_BF16, CfgMid64::TM, CfgMid64::TN, CfgMid64::THREADS},
 };
+const int kNumBf16Tiles = sizeof(kBf16Tiles) / sizeof(kBf16Tiles[0]);
 
 hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
   switch (id) {
     case 1: return launch<CfgLarge>(a, s);
     case 2: return launch<CfgMid>(a, s);
     case 3: return launch<CfgSmall>(a, s);
-    case 4: return launch<CfgWide>(a, s);
     case 5: return launch<CfgMid64>(a, s);
   }
   return hipErrorInvalidValue;
@@ -471,7 +475,6 @@ hipError_t occupancy_ffn_bf16(int id, int* n) {
     case 1: return occupancy<CfgLarge>(n);
     case 2: return occupancy<CfgMid>(n);
     case 3: return occupancy<CfgSmall>(n);
-    case 4: return occupancy<CfgWide>(n);
     case 5: return occupancy<CfgMid64>(n);
   }
   return hipErrorInvalidValue;
