@@ -151,15 +151,15 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     // tile is streamed once), the large block when experts are big
     const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
     const double sd = std::sqrt(avg);
-    int order[4] = {1, 2, 5, 3};
+    int order[6] = {7, 1, 6, 2, 5, 3};
     if (avg <= 24.0) {
-      order[0] = 3; order[1] = 5; order[2] = 2; order[3] = 1;
+      order[0] = 3; order[1] = 5; order[2] = 2; order[3] = 7;
     } else if (avg + 2.5 * sd <= 160.0) {
-      order[0] = 5; order[1] = 2; order[2] = 1; order[3] = 3;
+      order[0] = 5; order[1] = 2; order[2] = 7; order[3] = 3;
     } else if (avg + 4.0 * sd <= 192.0) {
-      order[0] = 2; order[1] = 5; order[2] = 1; order[3] = 3;
+      order[0] = 2; order[1] = 5; order[2] = 7; order[3] = 3;
     }
-    for (int i = 0; i < 4 && !t; ++i)
+    for (int i = 0; i < 6 && !t; ++i)
       if (tile_fits(find_tile(order[i]), s)) t = find_tile(order[i]);
     if (!t) return MOE_ERR_UNSUPPORTED;
   }

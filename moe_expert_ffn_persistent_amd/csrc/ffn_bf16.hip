@@ -436,6 +436,8 @@ using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill
 using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
 using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
 using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
+using CfgLarge64 = Cfg<256, 256, 2, 2, 64, 2>;   // 128x128, 128-byte rows, two stages
+using CfgLarge64w8 = Cfg<256, 256, 2, 4, 64, 2>; // 64x128 per wavefront, eight wavefronts
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -457,6 +459,8 @@ const TileInfo kBf16Tiles[] = {
     {2, MOE_BF16, CfgMid::TM, CfgMid::TN, CfgMid::THREADS},
     {3, MOE_BF16, CfgSmall::TM, CfgSmall::TN, CfgSmall::THREADS},
     {5, MOE_BF16, CfgMid64::TM, CfgMid64::TN, CfgMid64::THREADS},
+    {6, MOE_BF16, CfgLarge64::TM, CfgLarge64::TN, CfgLarge64::THREADS},
+    {7, MOE_BF16, CfgLarge64w8::TM, CfgLarge64w8::TN, CfgLarge64w8::THREADS},
 };
 const int kNumBf16Tiles = sizeof(kBf16Tiles) / sizeof(kBf16Tiles[0]);
 
@@ -466,6 +470,8 @@ hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
     case 2: return launch<CfgMid>(a, s);
     case 3: return launch<CfgSmall>(a, s);
     case 5: return launch<CfgMid64>(a, s);
+    case 6: return launch<CfgLarge64>(a, s);
+    case 7: return launch<CfgLarge64w8>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -476,6 +482,8 @@ hipError_t occupancy_ffn_bf16(int id, int* n) {
     case 2: return occupancy<CfgMid>(n);
     case 3: return occupancy<CfgSmall>(n);
     case 5: return occupancy<CfgMid64>(n);
+    case 6: return occupancy<CfgLarge64>(n);
+    case 7: return occupancy<CfgLarge64w8>(n);
   }
   return hipErrorInvalidValue;
 }

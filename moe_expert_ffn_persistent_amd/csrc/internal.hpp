@@ -28,7 +28,7 @@ struct LayoutArgs {
   int nchunks;
 };
 
-constexpr int kLayoutChunk = 1024;   // flat pairs per layout workgroup
+constexpr int kLayoutChunk = 256;    // flat pairs per layout workgroup
 constexpr int kTraceWords = 8;       // uint32 words per task record
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);

@@ -11,7 +11,7 @@
 // Kernels, all launched on the caller's stream, no host round trip:
 //   route_topk    one wavefront per token: k rounds of a wavefront argmax
 //                 over (z desc, index asc), softmax over the kept z.
-//   layout_count  one wavefront per chunk of 1024 flat pairs: per-expert
+//   layout_count  one wavefront per chunk of 256 flat pairs: per-expert
 //                 counts of the chunk.
 //   layout_scan   one workgroup: wavefront prefix scans over the chunk
 //                 counts of each expert (chunk bases), then over experts

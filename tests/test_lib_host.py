@@ -53,7 +53,7 @@ def test_abi_version_and_status_strings():
 def test_layout_scratch_bytes_host_only():
     _lib_or_skip()
     s = _lib.MoeShape(8, 512, 256, 8, 0, 32, 7168, 2048, 0)
-    chunks = -(-8 * 512 * 8 // 1024)
+    chunks = -(-8 * 512 * 8 // 256)
     assert _lib.layout_scratch_bytes(s) == chunks * 32 * 4
     bad = _lib.MoeShape(8, 512, 256, 8, 250, 32, 7168, 2048, 0)   # local range past E
     assert _lib.layout_scratch_bytes(bad) == 0
