@@ -14,6 +14,10 @@ extern const TileInfo kBf16Tiles[];
 extern const int kNumBf16Tiles;
 hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s);
 hipError_t occupancy_ffn_bf16(int id, int* n);
+extern const TileInfo kFp8Tiles[];
+extern const int kNumFp8Tiles;
+hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s);
+hipError_t occupancy_ffn_fp8(int id, int* n);
 
 namespace {
 
@@ -22,7 +26,7 @@ struct DeviceProps {
   bool ready = false;
   int cus = 0;
   int wall_khz = 0;
-  int occ[16] = {};
+  int occ[64] = {};
 };
 
 std::mutex g_mu;
@@ -43,6 +47,12 @@ int device_props(DeviceProps** out) {
       int n = 0;
       const int id = kBf16Tiles[i].id;
       if (occupancy_ffn_bf16(id, &n) != hipSuccess) return MOE_ERR_HIP;
+      p.occ[id] = n;
+    }
+    for (int i = 0; i < kNumFp8Tiles; ++i) {
+      int n = 0;
+      const int id = kFp8Tiles[i].id;
+      if (occupancy_ffn_fp8(id, &n) != hipSuccess) return MOE_ERR_HIP;
       p.occ[id] = n;
     }
     p.ready = true;
@@ -72,11 +82,17 @@ long long num_tokens(const moe_shape* s) { return (long long)s->num_slices * s->
 const TileInfo* find_tile(int id) {
   for (int i = 0; i < kNumBf16Tiles; ++i)
     if (kBf16Tiles[i].id == id) return &kBf16Tiles[i];
+  for (int i = 0; i < kNumFp8Tiles; ++i)
+    if (kFp8Tiles[i].id == id) return &kFp8Tiles[i];
   return nullptr;
 }
 
 bool tile_fits(const TileInfo* t, const moe_shape* s) {
-  return t && t->dtype == s->dtype && s->hidden % t->block_n == 0 && (2 * s->inter) % t->block_n == 0;
+  if (!t || t->dtype != s->dtype) return false;
+  if (s->hidden % t->block_n || (2 * s->inter) % t->block_n) return false;
+  // fp8: one 128-wide scale block per K stage, at most 128 blocks along H and I
+  if (s->dtype == MOE_FP8_E4M3 && (s->hidden / 128 > 128 || s->inter / 128 > 128)) return false;
+  return true;
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -135,7 +151,6 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     return MOE_ERR_INVALID_ARG;
   if (prm->lead_d < 0 || prm->grid < 0 || prm->experts_per_wave < 0 || prm->timeout_ms < 0)
     return MOE_ERR_INVALID_ARG;
-  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   DeviceProps* dp = nullptr;
   int st = device_props(&dp);
   if (st != MOE_OK) return st;
@@ -145,6 +160,10 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
     t = find_tile(prm->tile);
     if (!t) return MOE_ERR_INVALID_ARG;
     if (!tile_fits(t, s)) return MOE_ERR_UNSUPPORTED;
+  } else if (s->dtype == MOE_FP8_E4M3) {
+    for (int i = 0; i < kNumFp8Tiles && !t; ++i)
+      if (tile_fits(&kFp8Tiles[i], s)) t = &kFp8Tiles[i];
+    if (!t) return MOE_ERR_UNSUPPORTED;
   } else {
     // expected rows per local expert under uniform routing; pick the
     // smallest M-block that holds a typical expert whole (so each weight
@@ -232,9 +251,8 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
                         size_t ws_bytes, const moe_sched_params* prm, void* stream) {
   if (!shape_ok(s) || !lay || !prm || !x_slices || !comb || !w1 || !w2 || !ws)
     return MOE_ERR_INVALID_ARG;
-  (void)x_scales;
-  (void)w1_scales;
-  (void)w2_scales;
+  const bool fp8 = s->dtype == MOE_FP8_E4M3;
+  if (fp8 && (!x_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   moe_plan plan{};
   int st = moe_ffn_plan(s, prm, &plan);
   if (st != MOE_OK) return st;
@@ -245,7 +263,7 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   if (prm->trace && prm->trace_capacity < 1) return MOE_ERR_INVALID_ARG;
   if (num_tokens(s) == 0) return MOE_OK;
   for (int i = 0; i < s->num_slices; ++i)
-    if (!x_slices[i] || !comb[i]) return MOE_ERR_INVALID_ARG;
+    if (!x_slices[i] || !comb[i] || (fp8 && !x_scales[i])) return MOE_ERR_INVALID_ARG;
   DeviceProps* dp = nullptr;
   st = device_props(&dp);
   if (st != MOE_OK) return st;
@@ -287,7 +305,9 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   a.done = reinterpret_cast<int32_t*>(base + w.done);
   a.status = prm->status;
   a.trace = prm->trace;
-  return launch_ffn_bf16(plan.tile, a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  const hipError_t err = fp8 ? launch_ffn_fp8(plan.tile, a, (hipStream_t)stream)
+                             : launch_ffn_bf16(plan.tile, a, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, float* y,

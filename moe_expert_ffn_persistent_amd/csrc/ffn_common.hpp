@@ -1,0 +1,97 @@
+// Device helpers shared by the bf16 and fp8 persistent FFN kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+#include "sched.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct Meta {
+  int tile_off[MOE_MAX_LOCAL_EXPERTS + 1];
+  int wave_row[MOE_MAX_LOCAL_EXPERTS + 2];
+  const char* x[MOE_MAX_SLICES];
+  char* comb[MOE_MAX_SLICES];
+  int nwaves;
+  int flag;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+
+// Cache policy of a copy: kCacheNormal (weights and x rows; measured on
+// MI355X, non-temporal copies stream weights markedly slower), kStream (nt),
+// kCoherent (sc1, device scope: never served from a possibly stale L2 line of
+// this XCD) for h, which other XCDs produced during this launch.
+enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
+
+#ifndef MOE_WEIGHT_POLICY
+#define MOE_WEIGHT_POLICY kCacheNormal
+#endif
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+#ifndef MOE_H_COHERENT
+#define MOE_H_COHERENT 1
+#endif
+
+// One 1 KiB global->LDS copy for the wavefront: lane l's 16 bytes from src
+// land at LDS byte address m0 + 16*l. Issued from inline assembly so the
+// compiler does not serialise later LDS reads behind it; completion is
+// awaited explicitly with vm_wait and published with lds_barrier.
+template <int POL>
+__device__ __forceinline__ void dma16(const char* src, uint32_t m0) {
+  if constexpr (POL == kStream)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  else if constexpr (POL == kCoherent)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most NI*ahead of this wavefront's copies are outstanding
+template <int NI, int K>
+__device__ __forceinline__ void vm_wait_ahead(int ahead) {
+  if constexpr (K == 0) {
+    vm_wait<0>();
+  } else {
+    if (ahead >= K) vm_wait<NI * K>();
+    else vm_wait_ahead<NI, K - 1>(ahead);
+  }
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+
+// Four-byte direct-to-LDS copy: lane l's word lands at m0 + 4*l (inactive
+// lanes write nothing).
+template <int POL>
+__device__ __forceinline__ void dma4(const char* src, uint32_t m0) {
+  if constexpr (POL == kCoherent)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off sc1" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+
+}  // namespace moe

@@ -245,3 +245,67 @@ def test_h_handoff_across_calls_with_poisoned_workspace(tile):
             torch.cuda.synchronize()
             assert int(ffn.status.item()) == 0
             _check_against_oracle(up, ref)
+
+
+TOL_FP8 = 5e-2
+
+
+@pytest.mark.parametrize("H,I,T,L,k,E", [(256, 128, 32, 4, 2, 32), (512, 384, 100, 6, 4, 12),
+                                          (1024, 512, 96, 8, 4, 24), (768, 1280, 300, 3, 1, 3)])
+def test_fp8_block_scaled_both_schedules(H, I, T, L, k, E):
+    wl = _small_wl(hidden=H, inter=I, tokens_per_slice=T, num_local=L, top_k=k, num_experts=E,
+                   dtype="fp8", seed=8000 + H + I + T)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    print(f"[ffn] fp8 H={H} I={I} T={T} tile={ffn.plan.tile}", flush=True)
+    _route_and_layout(ffn, up)
+    outs = {}
+    for sched in ("expert_wave", "interleaved"):
+        up.reset_combine()
+        run_forward(ffn, up, schedule=sched)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        _check_against_oracle(up, ref, tol=TOL_FP8)
+        outs[sched] = up.combine_bits().copy()
+    assert (outs["expert_wave"] == outs["interleaved"]).all()
+
+
+@pytest.fixture(scope="module")
+def dsv3_full():
+    wl = mi.get_workload("dsv3")
+    return wl, mi.make_inputs(wl)
+
+
+@pytest.mark.parametrize("schedule", ["interleaved", "expert_wave"])
+def test_full_size_headline_sampled_rows(dsv3_full, schedule):
+    # the workload and launch configuration bench.py times (automatic plan),
+    # checked on sampled combine rows that the oracle evaluates one by one
+    wl, inp = dsv3_full
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    print(f"[ffn] full-size {wl.name} {schedule} tile={ffn.plan.tile} grid={ffn.plan.grid}", flush=True)
+    _route_and_layout(ffn, up)
+    run_forward(ffn, up, schedule=schedule)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    idx = ffn.layout_bufs.topk_idx.cpu().numpy()
+    w = ffn.layout_bufs.topk_w.cpu().numpy().astype(np.float64)
+    idx_ref, w_ref = mo.route(inp.logits, inp.bias, wl.top_k)
+    assert (idx == idx_ref).all() and np.abs(w - w_ref).max() <= 1e-6
+    lay = mo.dispatch_layout(idx_ref, wl.local_begin, wl.num_local, ffn.plan.block_m)
+    rng = np.random.default_rng(11)
+    pairs = []
+    for e in range(wl.num_local):   # first, last and two random rows of every expert
+        r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
+        if r1 > r0:
+            pairs += [int(lay.row_pair[r]) for r in {r0, r1 - 1, *rng.integers(r0, r1, 2)}]
+    want = mo.row_outputs(inp, idx_ref, w_ref, pairs)
+    C = up.combine_f64().reshape(-1, wl.hidden)
+    err = row_rel_err(C[pairs], want)
+    assert err.max() <= TOL_BF16, f"max per-row rel err {err.max():.3e}"
+    bits = up.combine_bits().reshape(-1, wl.hidden)
+    nonlocal_ = np.nonzero(lay.pair_row < 0)[0]
+    assert (bits[rng.choice(nonlocal_, 256, replace=False)] == 0xFFFF).all()
+    assert not (bits[lay.row_pair] == 0xFFFF).any()
