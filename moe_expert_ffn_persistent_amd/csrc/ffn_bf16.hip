@@ -282,16 +282,20 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, MOE_H_COHERENT && !l1);
     if (rec) rec[4] = (uint32_t)wall_clock64();
 
+    // Epilogues stage the output tile in LDS (the ring is free once every
+    // wavefront is past its last stage) and write whole rows: 16-byte stores,
+    // a row's bytes contiguous, instead of 8-byte pieces scattered over 32 rows.
+    lds_barrier();
     if (l1) {
-      // SwiGLU epilogue: h[p*TM + token][j0 + column] in bf16
-      char* hb = static_cast<char*>(a.h);
+      // SwiGLU: h[p*TM + token][j0 .. j0 + TN/2) in bf16
+      constexpr int HROW = C::TN;   // TN/2 columns x 2 bytes
+      static_assert(C::TM * HROW <= C::NS * C::STAGE_BYTES, "h staging fits the ring");
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
         const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
-        char* hrow = hb + ((size_t)p * C::TM + tok_l) * I * 2;
 #pragma unroll
         for (int fp = 0; fp < C::FB / 2; ++fp) {
-          const int col0 = j0 + (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
+          const int col0 = (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             float hv[4];
@@ -300,48 +304,62 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
               hv[i] = silu(tile.acc[2 * fp][tb][g4 * 4 + i]) * tile.acc[2 * fp + 1][tb][g4 * 4 + i];
             const uint64_t v = (uint64_t)pack_bf16x2(hv[0], hv[1]) |
                                ((uint64_t)pack_bf16x2(hv[2], hv[3]) << 32);
-            // device-scope store: written through this XCD's L2
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(hrow + (size_t)(col0 + g4 * 8) * 2), v,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *reinterpret_cast<uint64_t*>(lds + stage_off<HROW>(tok_l, (col0 + g4 * 8) * 2)) = v;
           }
         }
       }
-      // publish: every wavefront's device-scope h stores have completed
-      // (vmcnt drained) before the row counter moves
+      __syncthreads();
+      char* hb = static_cast<char*>(a.h) + ((size_t)p * C::TM * I + j0) * 2;
+      constexpr int NCH = HROW / 16;
+      for (int idx = tid; idx < C::TM * NCH; idx += C::THREADS) {
+        const int row = idx / NCH, c = idx - row * NCH;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<HROW>(row, c * 16));
+        // device scope: written through this XCD's L2 for the consuming XCD
+        store16<kCoherent>(hb + (size_t)row * I * 2 + c * 16, v);
+      }
+      // publish: every wavefront's h stores have completed before the row
+      // counter moves
       vm_wait<0>();
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (rec) rec[5] = (uint32_t)wall_clock64();
     } else {
-      // weighted combine stores
+      // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN
+      constexpr int CROW = C::TN * 2;
+      static_assert(C::TM * CROW <= C::NS * C::STAGE_BYTES, "combine staging fits the ring");
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
-        const int mm = m * C::TM + wt * C::TT + tb * 32 + (lane & 31);
-        if (mm < Me) {
-          const int r = r_base + mm;
-          const int f = a.row_pair[r];
-          const float w = a.row_weight[r];
-          const int tok = f / K;
-          const int j = f - tok * K;
-          const int s = tok / T;
-          char* dst = meta.comb[s] + ((size_t)(tok - s * T) * K + j) * H * 2;
+        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
+        const int mm = m * C::TM + tok_l;
+        const float w = mm < Me ? a.row_weight[r_base + mm] : 0.f;
 #pragma unroll
-          for (int fb = 0; fb < C::FB; ++fb) {
-            const int col0 = n * C::TN + wf * C::FT + fb * 32 + (lane >> 5) * 4;
+        for (int fb = 0; fb < C::FB; ++fb) {
+          const int col0 = wf * C::FT + fb * 32 + (lane >> 5) * 4;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const f32x16& v = tile.acc[fb][tb];
-              const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
-                                 ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
-              uint64_t* d = reinterpret_cast<uint64_t*>(dst + (size_t)(col0 + g4 * 8) * 2);
-              if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);   // not re-read by this kernel
-              else *d = o;
-            }
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16& v = tile.acc[fb][tb];
+            const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
+                               ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
+            *reinterpret_cast<uint64_t*>(lds + stage_off<CROW>(tok_l, (col0 + g4 * 8) * 2)) = o;
           }
         }
       }
+      __syncthreads();
+      constexpr int NCH = CROW / 16;
+      const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
+      for (int idx = tid; idx < rows * NCH; idx += C::THREADS) {
+        const int row = idx / NCH, c = idx - row * NCH;
+        const int f = a.row_pair[r_base + m * C::TM + row];
+        const int tok = f / K;
+        const int j = f - tok * K;
+        const int s = tok / T;
+        char* dst = meta.comb[s] + (((size_t)(tok - s * T) * K + j) * H + (size_t)n * C::TN) * 2;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<CROW>(row, c * 16));
+        if (MOE_COMBINE_NT) store16<kStream>(dst + c * 16, v);   // not re-read by this kernel
+        else store16<kCacheNormal>(dst + c * 16, v);
+      }
       if (rec) {
-        vm_wait<0>();   // the stamp covers the issue of this wavefront's stores
+        vm_wait<0>();   // the stamp covers the completion of this wavefront's stores
         rec[5] = (uint32_t)wall_clock64();
       }
     }

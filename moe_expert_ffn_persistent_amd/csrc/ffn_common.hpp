@@ -82,6 +82,29 @@ __device__ __forceinline__ void vm_wait_ahead(int ahead) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 
+// 16-byte store with a cache policy (inline assembly: completion is awaited
+// with vm_wait like the copies). kCoherent: device scope (sc1), written
+// through this XCD's L2; kStream: non-temporal.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <int POL>
+__device__ __forceinline__ void store16(void* dst, i32x4 v) {
+  if constexpr (POL == kCoherent)
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+  else if constexpr (POL == kStream)
+    asm volatile("global_store_dwordx4 %0, %1, off nt" ::"v"(dst), "v"(v) : "memory");
+  else
+    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "v"(v) : "memory");
+}
+
+// Epilogue staging in LDS: rows of ROWB bytes, 16-byte chunks XOR-swizzled
+// by the row so that a column of lanes (one row each) writes distinct banks
+// and a row of lanes reads whole rows back.
+template <int ROWB>
+__device__ __forceinline__ uint32_t stage_off(int row, int byte) {
+  constexpr int NCH = ROWB / 16;
+  return (uint32_t)(row * ROWB + ((((byte >> 4) ^ row) & (NCH - 1)) << 4) + (byte & 15));
+}
+
 // Four-byte direct-to-LDS copy: lane l's word lands at m0 + 4*l (inactive
 // lanes write nothing).
 template <int POL>
