@@ -71,7 +71,7 @@ struct Cfg {
   static_assert(CPR == 8 || CPR == 4, "rows of 64 or 128 bytes");
   static_assert(TN % RPI == 0 && TM % RPI == 0, "DMA instructions must not straddle operands");
   static_assert(((TN + TM) / RPI) % NW == 0, "DMA instructions must split evenly over wavefronts");
-  static_assert(NS >= 2 && NI * (NS - 2) <= 63, "vmcnt range");
+  static_assert(NS >= 2 && NI * (NS - 1) <= 63, "vmcnt range");
 };
 
 template <class C>
@@ -156,9 +156,18 @@ struct Tile {
       if (s < nk) issue(s, s, coherent);
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
-      lds_barrier();
-      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+      if (MOE_EARLY_ISSUE) {
+        // the copy of stage kt+NS-1 goes out before waiting for stage kt, so
+        // NS-1 stages are in flight during the wait (two barriers a stage)
+        if (kt > 0) lds_barrier();   // every wavefront is done with stage kt-1
+        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+        vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
+        lds_barrier();               // stage kt has landed for every wavefront
+      } else {
+        vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+        lds_barrier();
+        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+      }
       compute(lds + slot * C::STAGE_BYTES, wf, wt);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }

@@ -42,6 +42,9 @@ enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
 #ifndef MOE_COMBINE_NT
 #define MOE_COMBINE_NT 1
 #endif
+#ifndef MOE_EARLY_ISSUE
+#define MOE_EARLY_ISSUE 1
+#endif
 #ifndef MOE_H_COHERENT
 #define MOE_H_COHERENT 1
 #endif

@@ -45,7 +45,7 @@ struct Cfg8 {
   static_assert(TM == 32 * NW, "each wavefront copies the scales of 32 token rows");
   static_assert(TT % 32 == 0 && FT % 32 == 0 && FB % 2 == 0, "wavefront tile");
   static_assert(((TN + TM) / RPI) % NW == 0, "copies split evenly");
-  static_assert(NS >= 2 && NI * (NS - 2) <= 63, "vmcnt range");
+  static_assert(NS >= 2 && NI * (NS - 1) <= 63, "vmcnt range");
 };
 
 constexpr int kMaxKBlocks = 128;   // H/128 and I/128 limit
@@ -153,9 +153,16 @@ struct Tile8 {
       if (s < nk) issue(s, s, coherent);
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
-      lds_barrier();
-      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+      if (MOE_EARLY_ISSUE) {
+        if (kt > 0) lds_barrier();
+        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+        vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
+        lds_barrier();
+      } else {
+        vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+        lds_barrier();
+        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+      }
       compute(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
