@@ -115,7 +115,9 @@ typedef struct {
                                 (moe_plan.wall_clock_khz) at task start, after the
                                 dependency wait, after the mainloop, after the
                                 epilogue's stores were issued (Linear-2) or the row
-                                counter was published (Linear-1); words 6..7 = 0.
+                                counter was published (Linear-1); words 6..7 = low
+                                32 bits of the shader clock counter at task start
+                                and after the mainloop.
                                 Unused records stay untouched                          */
   int32_t trace_capacity;    /* records per workgroup                                      */
   int32_t debug_skip_l1_row; /* testing only: when >= 0, Linear-1 tiles of this scheduler

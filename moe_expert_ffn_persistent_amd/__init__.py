@@ -127,11 +127,48 @@ class MoeExpertFFN:
                              _stream(stream))
         return lb
 
+    def _check_buffers(self, x_slices, w1, w2, combine_slices, x_scales, w1_scales, w2_scales):
+        """The C ABI takes raw pointers; check sizes here so that a mismatch
+        (e.g. fp8 tensors given to a bf16 instance) raises instead of letting
+        a kernel read past a buffer."""
+        sh = self.shape
+        S, T, L, H, I, k = (sh.num_slices, sh.tokens_per_slice, sh.num_local_experts, sh.hidden,
+                            sh.inter, sh.top_k)
+        elt = 1 if self.dtype == "fp8" else 2
+
+        def need(t, nbytes, what):
+            if t is None:
+                raise ValueError(f"{what} is required")
+            if not t.is_cuda or t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+                raise ValueError(f"{what}: need a contiguous device tensor of at least {nbytes} bytes")
+
+        if len(x_slices) != S or len(combine_slices) != S:
+            raise ValueError(f"need {S} x slices and {S} combine slices")
+        for t in x_slices:
+            if t.element_size() != elt:
+                raise ValueError(f"x slices must have {elt}-byte elements for dtype {self.dtype}")
+            need(t, T * H * elt, "x slice")
+        for t in combine_slices:
+            need(t, T * k * H * 2, "combine slice")
+        for t, n, what in ((w1, L * 2 * I * H, "w1"), (w2, L * H * I, "w2")):
+            if t.element_size() != elt:
+                raise ValueError(f"{what} must have {elt}-byte elements for dtype {self.dtype}")
+            need(t, n * elt, what)
+        if self.dtype == "fp8":
+            if x_scales is None or len(x_scales) != S:
+                raise ValueError("fp8 needs one x-scale tensor per slice")
+            for t in x_scales:
+                need(t, T * (H // 128) * 4, "x scales")
+            need(w1_scales, L * (2 * I // 128) * (H // 128) * 4, "w1 scales")
+            need(w2_scales, L * (H // 128) * (I // 128) * 4, "w2 scales")
+
     def forward(self, x_slices, w1, w2, combine_slices, x_scales=None, w1_scales=None,
                 w2_scales=None, stream=None, **sched):
         """Run Linear-1 + SwiGLU and Linear-2 + weighted combine stores for
         every local expert, in the schedule given by ``sched`` (defaults from
         the constructor)."""
+        if self.num_tokens:
+            self._check_buffers(x_slices, w1, w2, combine_slices, x_scales, w1_scales, w2_scales)
         params = self.params(**sched)
         ptr = lambda t: None if t is None else t.data_ptr()
         _lib.ffn_forward(self.shape, self.layout_bufs.c_struct(),

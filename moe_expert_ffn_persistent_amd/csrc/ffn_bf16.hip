@@ -17,9 +17,8 @@
 //    the epilogue writes 8-byte pieces and one router weight per lane.
 //  - Both operands are K-contiguous in HBM (W[e] rows, x rows, h rows), so
 //    global->LDS copies move 16-byte chunks and each MFMA lane reads one
-//    16-byte chunk from LDS. LDS rows are BK*2 = 128 bytes; chunk c of row r
-//    is stored at chunk c ^ (r & 7) so the eight lanes of a read phase hit
-//    eight distinct bank groups.
+//    16-byte chunk from LDS. Chunks are XOR-swizzled by row so that a
+//    16-byte read of 16 consecutive rows touches 16 distinct bank groups.
 //  - Two LDS stages: the next stage's global loads are issued before the
 //    current stage's MFMAs and written to the other stage after them.
 //  - Linear-1 N-tiles interleave gate and up rows in 32-row blocks, so the
@@ -61,11 +60,17 @@ struct Cfg {
   static constexpr int ROW_BYTES = BK * 2;
   static constexpr int CPR = ROW_BYTES / 16;      // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;            // rows per 1 KiB DMA instruction
-  static constexpr int SWZ_SHIFT = CPR == 8 ? 0 : 1;
+  // chunk c of row r is stored at chunk c ^ ((r >> SWZ_SHIFT) & SWZ_MASK): the
+  // 16 lanes served per LDS clock (16-byte reads of rows r..r+15 at one
+  // logical chunk) then hit 16 distinct 16-byte bank groups of the 256-byte
+  // bank space
+  static constexpr int SWZ_SHIFT = CPR == 8 ? 1 : 2;
   static constexpr int SWZ_MASK = CPR - 1;
   static constexpr int NI = (TN + TM) / RPI / NW; // DMA instructions per wavefront per stage
   static constexpr int A_BYTES = TN * ROW_BYTES;
   static constexpr int STAGE_BYTES = (TN + TM) * ROW_BYTES;
+  // LDS: the copy ring, reused by the epilogue to stage a TM x TN bf16 tile
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES > TM * TN * 2 ? NS * STAGE_BYTES : TM * TN * 2;
   static_assert(TT % 32 == 0 && FT % 32 == 0, "wavefront tile must be a multiple of 32");
   static_assert(FB % 2 == 0, "gate/up pairing needs an even number of feature blocks");
   static_assert(CPR == 8 || CPR == 4, "rows of 64 or 128 bytes");
@@ -113,31 +118,53 @@ struct Tile {
     }
   }
 
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt) {
+  __device__ __forceinline__ void load_frags(const char* stage, int ks, int wf, int wt,
+                                             bf16x8 (&af)[C::FB], bf16x8 (&bf)[C::TB]) {
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
-    const int half = lane >> 5;
     const int swz = (r_lane >> C::SWZ_SHIFT) & C::SWZ_MASK;
+    const int chunk = ((2 * ks + (lane >> 5)) ^ swz) << 4;
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      const int chunk = ((2 * ks + half) ^ swz) << 4;
-      bf16x8 af[C::FB], bf[C::TB];
+    for (int fb = 0; fb < C::FB; ++fb) {
+      const int r = wf * C::FT + fb * 32 + r_lane;
+      af[fb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + r * C::ROW_BYTES + chunk));
+    }
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) {
-        const int r = wf * C::FT + fb * 32 + r_lane;
-        af[fb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + r * C::ROW_BYTES + chunk));
-      }
+    for (int tb = 0; tb < C::TB; ++tb) {
+      const int r = wt * C::TT + tb * 32 + r_lane;
+      bf[tb] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(stage + C::A_BYTES + r * C::ROW_BYTES + chunk));
+    }
+  }
+
+  // One stage: the fragments of k-step ks+1 are read from LDS while the
+  // MFMAs of k-step ks run (register double buffering); the MFMA / LDS-read
+  // interleaving is pinned so the reads are not sunk next to their use.
+  __device__ __forceinline__ void compute(const char* stage, int wf, int wt) {
+    constexpr int KS = C::BK / 16;
+    constexpr int NM = C::FB * C::TB;   // MFMAs per k-step
+    constexpr int NL = C::FB + C::TB;   // LDS reads per k-step
+    bf16x8 af[2][C::FB], bf[2][C::TB];
+    load_frags(stage, 0, wf, wt, af[0], bf[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NL, 0);   // k-step 0 reads first
 #pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        const int r = wt * C::TT + tb * 32 + r_lane;
-        bf[tb] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(stage + C::A_BYTES + r * C::ROW_BYTES + chunk));
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) load_frags(stage, ks + 1, wf, wt, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
       for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
         for (int tb = 0; tb < C::TB; ++tb)
-          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fb], bf[tb], acc[fb][tb], 0, 0, 0);
+          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fb], bf[cur][tb], acc[fb][tb], 0, 0, 0);
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+          if (i < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
   }
 
@@ -176,7 +203,7 @@ struct Tile {
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   __shared__ Meta meta;
 
   const int tid = threadIdx.x;
@@ -224,8 +251,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       rec[0] = (uint32_t)t.kind | ((uint32_t)n << 2);
       rec[1] = (uint32_t)p;
       rec[2] = (uint32_t)wall_clock64();
-      rec[6] = 0u;
-      rec[7] = 0u;
+      rec[6] = (uint32_t)__builtin_readcyclecounter();   // shader clock
     }
     ++seq;
     const int e = expert_of_row(meta.tile_off, L, p);
@@ -289,7 +315,10 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
     }
     tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, MOE_H_COHERENT && !l1);
-    if (rec) rec[4] = (uint32_t)wall_clock64();
+    if (rec) {
+      rec[4] = (uint32_t)wall_clock64();
+      rec[7] = (uint32_t)__builtin_readcyclecounter();
+    }
 
     // Epilogues stage the output tile in LDS (the ring is free once every
     // wavefront is past its last stage) and write whole rows: 16-byte stores,
@@ -298,7 +327,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     if (l1) {
       // SwiGLU: h[p*TM + token][j0 .. j0 + TN/2) in bf16
       constexpr int HROW = C::TN;   // TN/2 columns x 2 bytes
-      static_assert(C::TM * HROW <= C::NS * C::STAGE_BYTES, "h staging fits the ring");
+      static_assert(C::TM * HROW <= C::LDS_BYTES, "h staging fits");
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
         const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
@@ -335,7 +364,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     } else {
       // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN
       constexpr int CROW = C::TN * 2;
-      static_assert(C::TM * CROW <= C::NS * C::STAGE_BYTES, "combine staging fits the ring");
+      static_assert(C::TM * CROW <= C::LDS_BYTES, "combine staging fits");
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
         const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
@@ -396,6 +425,8 @@ using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
 using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
 using CfgLarge64 = Cfg<256, 256, 2, 2, 64, 2>;   // 128x128, 128-byte rows, two stages
 using CfgLarge64w8 = Cfg<256, 256, 2, 4, 64, 2>; // 64x128 per wavefront, eight wavefronts
+using CfgLarge32w8 = Cfg<256, 256, 2, 4, 32, 4>; // as 7 with 64-byte rows and four stages
+using CfgLarge32w8s3 = Cfg<256, 256, 2, 4, 32, 3>;
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -419,6 +450,8 @@ const TileInfo kBf16Tiles[] = {
     {5, MOE_BF16, CfgMid64::TM, CfgMid64::TN, CfgMid64::THREADS},
     {6, MOE_BF16, CfgLarge64::TM, CfgLarge64::TN, CfgLarge64::THREADS},
     {7, MOE_BF16, CfgLarge64w8::TM, CfgLarge64w8::TN, CfgLarge64w8::THREADS},
+    {8, MOE_BF16, CfgLarge32w8::TM, CfgLarge32w8::TN, CfgLarge32w8::THREADS},
+    {9, MOE_BF16, CfgLarge32w8s3::TM, CfgLarge32w8s3::TN, CfgLarge32w8s3::THREADS},
 };
 const int kNumBf16Tiles = sizeof(kBf16Tiles) / sizeof(kBf16Tiles[0]);
 
@@ -430,6 +463,8 @@ hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
     case 5: return launch<CfgMid64>(a, s);
     case 6: return launch<CfgLarge64>(a, s);
     case 7: return launch<CfgLarge64w8>(a, s);
+    case 8: return launch<CfgLarge32w8>(a, s);
+    case 9: return launch<CfgLarge32w8s3>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -442,6 +477,8 @@ hipError_t occupancy_ffn_bf16(int id, int* n) {
     case 5: return occupancy<CfgMid64>(n);
     case 6: return occupancy<CfgLarge64>(n);
     case 7: return occupancy<CfgLarge64w8>(n);
+    case 8: return occupancy<CfgLarge32w8>(n);
+    case 9: return occupancy<CfgLarge32w8s3>(n);
   }
   return hipErrorInvalidValue;
 }

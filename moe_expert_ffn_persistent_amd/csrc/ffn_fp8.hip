@@ -65,7 +65,7 @@ struct Tile8 {
     for (int i = 0; i < C::NID; ++i) {
       const int j = wave + C::NW * i;
       const int r = j * C::RPI + lane / C::CPR;
-      const int c = (lane % C::CPR) ^ (r & 7);
+      const int c = (lane % C::CPR) ^ ((r >> 1) & 7);   // see the bf16 kernel's swizzle
       const char* base = j * C::RPI < C::TN ? wrow(r) : trow(r - C::TN);
       src[i] = base + c * 16;
     }
@@ -96,7 +96,7 @@ struct Tile8 {
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
     const int half = lane >> 5;
-    const int swz = r_lane & 7;
+    const int swz = (r_lane >> 1) & 7;
     f32x16 part[C::FB][C::TB];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -230,8 +230,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       rec[0] = (uint32_t)t.kind | ((uint32_t)n << 2);
       rec[1] = (uint32_t)p;
       rec[2] = (uint32_t)wall_clock64();
-      rec[6] = 0u;
-      rec[7] = 0u;
+      rec[6] = (uint32_t)__builtin_readcyclecounter();   // shader clock
     }
     ++seq;
     const int e = expert_of_row(meta.tile_off, L, p);
@@ -308,7 +307,10 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
                  [&](int q) { return hsb + ((size_t)p * C::TM + q) * IB * 4; });
     }
     tile.mainloop(lds, nk, wf, wt, MOE_H_COHERENT && !l1, meta8.wsc, l1);
-    if (rec) rec[4] = (uint32_t)wall_clock64();
+    if (rec) {
+      rec[4] = (uint32_t)wall_clock64();
+      rec[7] = (uint32_t)__builtin_readcyclecounter();
+    }
 
     if (l1) {
       // SwiGLU, per-token amax over the tile's 128 h columns, e4m3 h + scale

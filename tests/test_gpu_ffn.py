@@ -309,3 +309,22 @@ def test_full_size_headline_sampled_rows(dsv3_full, schedule):
     nonlocal_ = np.nonzero(lay.pair_row < 0)[0]
     assert (bits[rng.choice(nonlocal_, 256, replace=False)] == 0xFFFF).all()
     assert not (bits[lay.row_pair] == 0xFFFF).any()
+
+
+def test_wrapper_rejects_mismatched_buffers_before_launch():
+    # fp8-sized (1-byte) tensors given to a bf16 instance, or short buffers,
+    # raise in the binding instead of reaching a kernel that would read past
+    # their ends
+    wl = mi.get_workload("tiny")
+    ffn = make_ffn(wl)
+    up = Uploaded(mi.make_inputs(wl))
+    _route_and_layout(ffn, up)
+    x8 = [torch.zeros_like(t, dtype=torch.uint8) for t in up.x_slices]
+    with pytest.raises(ValueError):
+        ffn.forward(x8, up.w1, up.w2, up.comb_slices)
+    with pytest.raises(ValueError):
+        ffn.forward(up.x_slices, up.w1[:1], up.w2, up.comb_slices)
+    with pytest.raises(ValueError):
+        ffn.forward(up.x_slices[:-1], up.w1, up.w2, up.comb_slices)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
