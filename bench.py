@@ -32,7 +32,7 @@ import moe_inputs as mi  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-FFN_KERNEL = "moe_ffn_bf16"
+FFN_KERNELS = {"bf16": "moe_ffn_bf16", "fp8": "moe_ffn_fp8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -196,11 +196,14 @@ def main():
             per[sched].append(a_.elapsed_time(b_))
     sched_out = {}
     for s_, v in per.items():
+        if not v:
+            continue
         med = statistics.median(v)
         sched_out[s_] = {"ffn_us_median": round(med * 1e3, 2), "ffn_us_min": round(min(v) * 1e3, 2),
                          "tflops": round(flops / (med * 1e-3) / 1e12, 2),
                          "hbm_gbs": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
-    speedup = statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
+    speedup = (statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
+               if per["interleaved"] else None)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -231,7 +234,7 @@ def main():
         achieved = flops / ffn_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4), "traffic": traffic}
-    roof.update({"kernel": FFN_KERNEL, "avg_launch_us": round(ffn_avg_s * 1e6, 2),
+    roof.update({"kernel": FFN_KERNELS[wl.dtype], "avg_launch_us": round(ffn_avg_s * 1e6, 2),
                  "algorithmic_bytes": alg_bytes, "algorithmic_flops": flops,
                  "bytes_parts": byte_parts,
                  "mfma_frac": round(flops / ffn_avg_s / 1e12 / peak_flops, 4),
@@ -264,7 +267,7 @@ def main():
         "pct_of_mfma_peak": round(100 * flops / (ms_per_step * 1e-3) / 1e12 / peak_flops, 2),
         "ffn_only_ms": round(statistics.mean(ffn_ms), 4),
         "per_schedule": sched_out,
-        "speedup_interleaved_over_wave": round(speedup, 4),
+        "speedup_interleaved_over_wave": None if speedup is None else round(speedup, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),

@@ -66,11 +66,13 @@ class MoeError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load the HIP library; raises if it has not been built."""
+def load(path: str | None = None):
+    """Load the HIP library (``LIB_PATH`` unless a path is given); raises if
+    it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m moe_expert_ffn_persistent_amd.build`")

@@ -19,8 +19,9 @@
 //    global->LDS copies move 16-byte chunks and each MFMA lane reads one
 //    16-byte chunk from LDS. Chunks are XOR-swizzled by row so that a
 //    16-byte read of 16 consecutive rows touches 16 distinct bank groups.
-//  - Two LDS stages: the next stage's global loads are issued before the
-//    current stage's MFMAs and written to the other stage after them.
+//  - An NS-stage LDS ring filled by direct-to-LDS copies: the copy of stage
+//    kt+NS-1 is issued between the MFMAs of stage kt (spread over the first
+//    half of them), one workgroup barrier per stage.
 //  - Linear-1 N-tiles interleave gate and up rows in 32-row blocks, so the
 //    gate and up accumulators of one output column sit in the same lane.
 //  - h and l2_full cross XCDs (each XCD has its own L2): the producer writes
@@ -67,6 +68,11 @@ struct Cfg {
   static constexpr int SWZ_SHIFT = CPR == 8 ? 1 : 2;
   static constexpr int SWZ_MASK = CPR - 1;
   static constexpr int NI = (TN + TM) / RPI / NW; // DMA instructions per wavefront per stage
+  static constexpr int NIW = TN / RPI / NW;       // of which weight rows (the first NIW)
+  static constexpr int NM = (BK / 16) * (TT / 32) * (FT / 32);   // MFMAs per wavefront per stage
+  // copy instruction i of a stage is issued after MFMA issue_slot(i) of the
+  // stage before: spread evenly over the first MOE_ISSUE_SPREAD/8 of the MFMAs
+  static constexpr int issue_slot(int i) { return i * NM * MOE_ISSUE_SPREAD / (NI * 8); }
   static constexpr int A_BYTES = TN * ROW_BYTES;
   static constexpr int STAGE_BYTES = (TN + TM) * ROW_BYTES;
   // LDS: the copy ring, reused by the epilogue to stage a TM x TN bf16 tile
@@ -76,6 +82,7 @@ struct Cfg {
   static_assert(CPR == 8 || CPR == 4, "rows of 64 or 128 bytes");
   static_assert(TN % RPI == 0 && TM % RPI == 0, "DMA instructions must not straddle operands");
   static_assert(((TN + TM) / RPI) % NW == 0, "DMA instructions must split evenly over wavefronts");
+  static_assert(TN % (RPI * NW) == 0, "every wavefront copies weight rows in its first NIW instructions");
   static_assert(NS >= 2 && NI * (NS - 1) <= 63, "vmcnt range");
 };
 
@@ -102,100 +109,103 @@ struct Tile {
     }
   }
 
-  // WPOL / TPOL: cache policy of the weight / token rows
-  // weight rows use MOE_WEIGHT_POLICY; token rows are copied with
-  // device-scope loads when `coherent` (h written during this launch)
-  __device__ __forceinline__ void issue(int kt, int slot, bool coherent) {
+  // One 1 KiB copy (instruction i of this wavefront) of the stage at byte
+  // offset `off` of the rows into the ring slot at LDS address `slot`.
+  // Instructions below NIW fill weight rows, the rest token rows; token rows
+  // are h (written during this launch by other XCDs) when COH, copied with
+  // device-scope loads.
+  template <bool COH>
+  __device__ __forceinline__ void issue_one(int i, size_t off, uint32_t slot) {
     const int wave = threadIdx.x >> 6;
-    const size_t off = (size_t)kt * C::ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-      const int j = wave + C::NW * i;
-      const uint32_t dst = uni(ring + slot * C::STAGE_BYTES + j * 1024);
-      if (j * C::RPI < C::TN) dma16<MOE_WEIGHT_POLICY>(src[i] + off, dst);
-      else if (coherent) dma16<kCoherent>(src[i] + off, dst);
-      else dma16<kCacheNormal>(src[i] + off, dst);
-    }
+    const uint32_t dst = uni(slot + (wave + C::NW * i) * 1024);
+    if (i < C::NIW) dma16<MOE_WEIGHT_POLICY>(src[i] + off, dst);
+    else if (COH) dma16<kCoherent>(src[i] + off, dst);
+    else dma16<kCacheNormal>(src[i] + off, dst);
   }
 
-  __device__ __forceinline__ void load_frags(const char* stage, int ks, int wf, int wt,
-                                             bf16x8 (&af)[C::FB], bf16x8 (&bf)[C::TB]) {
+  // fragment q of k-step ks: q < FB are weight (A) fragments, the rest token
+  // (B) fragments; lane l reads row l%32 of its 32-row block, 16 bytes at
+  // logical chunk 2*ks + l/32
+  __device__ __forceinline__ void load_frag(const char* stage, int ks, int q, int wf, int wt,
+                                            bf16x8 (&af)[C::FB], bf16x8 (&bf)[C::TB]) {
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
     const int swz = (r_lane >> C::SWZ_SHIFT) & C::SWZ_MASK;
     const int chunk = ((2 * ks + (lane >> 5)) ^ swz) << 4;
-#pragma unroll
-    for (int fb = 0; fb < C::FB; ++fb) {
-      const int r = wf * C::FT + fb * 32 + r_lane;
-      af[fb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + r * C::ROW_BYTES + chunk));
-    }
-#pragma unroll
-    for (int tb = 0; tb < C::TB; ++tb) {
-      const int r = wt * C::TT + tb * 32 + r_lane;
-      bf[tb] = __builtin_bit_cast(
+    if (q < C::FB) {
+      const int r = wf * C::FT + q * 32 + r_lane;
+      af[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(stage + r * C::ROW_BYTES + chunk));
+    } else {
+      const int r = wt * C::TT + (q - C::FB) * 32 + r_lane;
+      bf[q - C::FB] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const uint4*>(stage + C::A_BYTES + r * C::ROW_BYTES + chunk));
     }
   }
 
-  // One stage: the fragments of k-step ks+1 are read from LDS while the
-  // MFMAs of k-step ks run (register double buffering); the MFMA / LDS-read
-  // interleaving is pinned so the reads are not sunk next to their use.
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt) {
+  // One stage of MFMAs with the copy of a later stage spread between them.
+  // Program order is fixed: after MFMA m of k-step ks come the fragment reads
+  // of k-step ks+1 assigned to m (register double buffering) and the copies
+  // assigned to MFMA ks*NMF+m. Measured on MI355X, copies issued in one burst
+  // hold the wavefront at the issue until the address unit drains them, so the
+  // copy and the MFMAs of a stage run back to back; spread between the MFMAs
+  // they overlap.
+  template <bool COH>
+  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, bool issue, size_t off,
+                                          uint32_t slot) {
     constexpr int KS = C::BK / 16;
-    constexpr int NM = C::FB * C::TB;   // MFMAs per k-step
-    constexpr int NL = C::FB + C::TB;   // LDS reads per k-step
+    constexpr int NMF = C::FB * C::TB;   // MFMAs per k-step
+    constexpr int NL = C::FB + C::TB;    // fragment reads per k-step
     bf16x8 af[2][C::FB], bf[2][C::TB];
-    load_frags(stage, 0, wf, wt, af[0], bf[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, NL, 0);   // k-step 0 reads first
+#pragma unroll
+    for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < KS) load_frags(stage, ks + 1, wf, wt, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb)
+      for (int m = 0; m < NMF; ++m) {
+        const int fb = m / C::TB, tb = m % C::TB;
+        acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fb], bf[cur][tb], acc[fb][tb], 0, 0, 0);
+        if (ks + 1 < KS) {
 #pragma unroll
-        for (int tb = 0; tb < C::TB; ++tb)
-          acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fb], bf[cur][tb], acc[fb][tb], 0, 0, 0);
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
-          if (i < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          for (int q = 0; q < NL; ++q)
+            if ((q < NMF ? q : NMF - 1) == m) load_frag(stage, ks + 1, q, wf, wt, af[cur ^ 1], bf[cur ^ 1]);
         }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        if (issue) {
+#pragma unroll
+          for (int i = 0; i < C::NI; ++i)
+            if (C::issue_slot(i) == ks * NMF + m) issue_one<COH>(i, off, slot);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // Full K loop over nk stages of BK through an NS-stage LDS ring: stage kt
-  // is awaited (own copies, then the workgroup barrier), the copy of stage
-  // kt+NS-1 is issued into the slot stage kt-1 used, then stage kt is
-  // multiplied. acc starts at zero.
-  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, bool coherent) {
+  // Full K loop over nk stages of BK through an NS-stage LDS ring. Stage kt
+  // is awaited (own copies, then one workgroup barrier, after which every
+  // wavefront is also done with stage kt-1), then multiplied while the copy of
+  // stage kt+NS-1 goes into the slot stage kt-1 used. acc starts at zero.
+  template <bool COH>
+  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) acc[fb][tb] = f32x16{};
-    lds_barrier();   // every wavefront is done reading the ring of the previous tile
+    lds_barrier();   // every wavefront is done with the LDS of the previous tile
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
-      if (s < nk) issue(s, s, coherent);
+      if (s < nk) {
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, (size_t)s * C::ROW_BYTES, ring + s * C::STAGE_BYTES);
+      }
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      if (MOE_EARLY_ISSUE) {
-        // the copy of stage kt+NS-1 goes out before waiting for stage kt, so
-        // NS-1 stages are in flight during the wait (two barriers a stage)
-        if (kt > 0) lds_barrier();   // every wavefront is done with stage kt-1
-        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
-        vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
-        lds_barrier();               // stage kt has landed for every wavefront
-      } else {
-        vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
-        lds_barrier();
-        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
-      }
-      compute(lds + slot * C::STAGE_BYTES, wf, wt);
+      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+      lds_barrier();
+      const int nxt = kt + C::NS - 1;
+      const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
+      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, nxt < nk, (size_t)nxt * C::ROW_BYTES,
+                   ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
   }
@@ -314,7 +324,9 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; },
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
     }
-    tile.mainloop(lds, (l1 ? H : I) / C::BK, wf, wt, MOE_H_COHERENT && !l1);
+    const int nk = (l1 ? H : I) / C::BK;
+    if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt);
+    else tile.template mainloop<true>(lds, nk, wf, wt);
     if (rec) {
       rec[4] = (uint32_t)wall_clock64();
       rec[7] = (uint32_t)__builtin_readcyclecounter();

@@ -42,8 +42,8 @@ enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
 #ifndef MOE_COMBINE_NT
 #define MOE_COMBINE_NT 1
 #endif
-#ifndef MOE_EARLY_ISSUE
-#define MOE_EARLY_ISSUE 1
+#ifndef MOE_ISSUE_SPREAD
+#define MOE_ISSUE_SPREAD 4   // eighths of a stage's MFMAs over which the next copy is spread
 #endif
 #ifndef MOE_H_COHERENT
 #define MOE_H_COHERENT 1

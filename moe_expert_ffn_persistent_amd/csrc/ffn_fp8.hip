@@ -153,16 +153,11 @@ struct Tile8 {
       if (s < nk) issue(s, s, coherent);
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      if (MOE_EARLY_ISSUE) {
-        if (kt > 0) lds_barrier();
-        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
-        vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
-        lds_barrier();
-      } else {
-        vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
-        lds_barrier();
-        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
-      }
+      // the copy of stage kt+NS-1 goes out before waiting for stage kt
+      if (kt > 0) lds_barrier();   // every wavefront is done with stage kt-1
+      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
+      vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
+      lds_barrier();               // stage kt has landed for every wavefront
       compute(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
