@@ -215,6 +215,11 @@ template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   __shared__ Meta meta;
+  // combine row destinations of the current Linear-2 task: past the staged
+  // tile in the ring when there is room, else an array of their own
+  constexpr bool kRowDstInRing = C::TM * C::TN * 2 + C::TM * (int)sizeof(char*) <= C::LDS_BYTES;
+  __shared__ char* rowdst_s[kRowDstInRing ? 1 : C::TM];
+  char** const rowdst = kRowDstInRing ? reinterpret_cast<char**>(lds + C::TM * C::TN * 2) : rowdst_s;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -374,9 +379,19 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (rec) rec[5] = (uint32_t)wall_clock64();
     } else {
-      // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN
+      // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN.
+      // Destinations first (one row per thread, independent loads that
+      // overlap the staging), so the store loop below waits on no load.
       constexpr int CROW = C::TN * 2;
       static_assert(C::TM * CROW <= C::LDS_BYTES, "combine staging fits");
+      const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
+      for (int row = tid; row < rows; row += C::THREADS) {
+        const int f = a.row_pair[r_base + m * C::TM + row];
+        const int tok = f / K;
+        const int j = f - tok * K;
+        const int s = tok / T;
+        rowdst[row] = meta.comb[s] + (((size_t)(tok - s * T) * K + j) * H + (size_t)n * C::TN) * 2;
+      }
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
         const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
@@ -396,14 +411,9 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       }
       __syncthreads();
       constexpr int NCH = CROW / 16;
-      const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
       for (int idx = tid; idx < rows * NCH; idx += C::THREADS) {
         const int row = idx / NCH, c = idx - row * NCH;
-        const int f = a.row_pair[r_base + m * C::TM + row];
-        const int tok = f / K;
-        const int j = f - tok * K;
-        const int s = tok / T;
-        char* dst = meta.comb[s] + (((size_t)(tok - s * T) * K + j) * H + (size_t)n * C::TN) * 2;
+        char* dst = rowdst[row];
         const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<CROW>(row, c * 16));
         if (MOE_COMBINE_NT) store16<kStream>(dst + c * 16, v);   // not re-read by this kernel
         else store16<kCacheNormal>(dst + c * 16, v);

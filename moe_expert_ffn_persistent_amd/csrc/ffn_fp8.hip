@@ -37,14 +37,21 @@ struct Cfg8 {
   static constexpr int ROW_BYTES = 128;                 // one 128-element K block of e4m3
   static constexpr int CPR = 8, RPI = 8;
   static constexpr int NID = (TN + TM) / RPI / NW;      // operand copies per wavefront per stage
+  static constexpr int NIW = TN / RPI / NW;             // of which weight rows (the first NIW)
   static constexpr int NI = NID + 1;                    // plus one token-scale copy
   static constexpr int A_BYTES = TN * ROW_BYTES;
+  // token scales: wavefront w copies the scales of rows (64w + lane) mod TM
+  // into its own 256-byte slot, so row q's scale sits at word q
   static constexpr int SCALE_OFF = (TN + TM) * ROW_BYTES;
   static constexpr int STAGE_BYTES = SCALE_OFF + NW * 256;
+  static constexpr int NM = 2 * FB * TB;                // MFMAs per wavefront per stage
+  // copy i of a stage is issued after MFMA issue_slot(i) of the stage before
+  static constexpr int issue_slot(int i) { return i * NM * MOE_ISSUE_SPREAD / (NI * 8); }
   static_assert(TN == 256, "an N-tile must own exactly one 128-column h-scale block");
-  static_assert(TM == 32 * NW, "each wavefront copies the scales of 32 token rows");
+  static_assert(TM % 64 == 0 && TM <= 64 * NW, "token-scale copies cover the M-block");
   static_assert(TT % 32 == 0 && FT % 32 == 0 && FB % 2 == 0, "wavefront tile");
   static_assert(((TN + TM) / RPI) % NW == 0, "copies split evenly");
+  static_assert(TN % (RPI * NW) == 0, "every wavefront copies weight rows in its first NIW instructions");
   static_assert(NS >= 2 && NI * (NS - 1) <= 63, "vmcnt range");
 };
 
@@ -69,68 +76,86 @@ struct Tile8 {
       const char* base = j * C::RPI < C::TN ? wrow(r) : trow(r - C::TN);
       src[i] = base + c * 16;
     }
-    ssrc = srow(wave * 32 + (lane & 31));   // lanes l and l+32 copy the same scale
+    ssrc = srow((wave * 64 + lane) % C::TM);
   }
 
-  __device__ __forceinline__ void issue(int kt, int slot, bool coherent) {
+  // copy i of stage kt into the ring slot at LDS address `slot`: operand
+  // rows (weights first), then the token scales
+  template <bool COH>
+  __device__ __forceinline__ void issue_one(int i, int kt, uint32_t slot) {
     const int wave = threadIdx.x >> 6;
-    const uint32_t stage = ring + slot * C::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::NID; ++i) {
-      const int j = wave + C::NW * i;
-      const uint32_t dst = uni(stage + j * 1024);
-      const char* s = src[i] + (size_t)kt * C::ROW_BYTES;
-      if (j * C::RPI < C::TN) dma16<kCacheNormal>(s, dst);
-      else if (coherent) dma16<kCoherent>(s, dst);
-      else dma16<kCacheNormal>(s, dst);
+    if (i < C::NID) {
+      const uint32_t dst = uni(slot + (wave + C::NW * i) * 1024);
+      const char* sp = src[i] + (size_t)kt * C::ROW_BYTES;
+      if (i < C::NIW) dma16<MOE_WEIGHT_POLICY>(sp, dst);
+      else if (COH) dma16<kCoherent>(sp, dst);
+      else dma16<kCacheNormal>(sp, dst);
+    } else {
+      const uint32_t dst = uni(slot + C::SCALE_OFF + wave * 256);
+      if (COH) dma4<kCoherent>(ssrc + kt * 4, dst);
+      else dma4<kCacheNormal>(ssrc + kt * 4, dst);
     }
-    const uint32_t sdst = uni(stage + C::SCALE_OFF + wave * 256);
-    if (coherent) dma4<kCoherent>(ssrc + kt * 4, sdst);
-    else dma4<kCacheNormal>(ssrc + kt * 4, sdst);
   }
 
-  // one 128-wide K block: two MFMAs into a partial tile, then promotion with
-  // the block's token and weight scales (sw: LDS, [2][kMaxKBlocks])
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt,
-                                          const float* sw, bool l1) {
+  // fragment q (q < FB: weights, else tokens) of MFMA step mi: 32 K-elements
+  // per lane from two swizzled 16-byte chunks
+  __device__ __forceinline__ void load_frag(const char* stage, int mi, int q, int wf, int wt,
+                                            i32x8 (&af)[C::FB], i32x8 (&bf)[C::TB]) {
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
-    const int half = lane >> 5;
     const int swz = (r_lane >> 1) & 7;
+    const int c0 = 4 * mi + 2 * (lane >> 5);
+    const int o0 = (c0 ^ swz) << 4, o1 = ((c0 + 1) ^ swz) << 4;
+    const char* row = q < C::FB ? stage + (wf * C::FT + q * 32 + r_lane) * C::ROW_BYTES
+                                : stage + C::A_BYTES + (wt * C::TT + (q - C::FB) * 32 + r_lane) * C::ROW_BYTES;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + o0);
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + o1);
+    const i32x8 v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if (q < C::FB) af[q] = v;
+    else bf[q - C::FB] = v;
+  }
+
+  // one 128-wide K block: two MFMAs per output block into a partial tile
+  // (the copy of a later stage spread between them, fragments of the second
+  // step read during the first), then promotion with the block's token and
+  // weight scales (sw: LDS, [2][kMaxKBlocks])
+  template <bool COH>
+  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
+                                          bool l1, bool issue, int kt_next, uint32_t slot) {
+    constexpr int NMF = C::FB * C::TB;
+    constexpr int NL = C::FB + C::TB;
+    const int lane = threadIdx.x & 63;
+    const int r_lane = lane & 31;
+    i32x8 af[2][C::FB], bf[2][C::TB];
     f32x16 part[C::FB][C::TB];
 #pragma unroll
+    for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-      const int c0 = 4 * mi + 2 * half;
-      const int o0 = (c0 ^ swz) << 4, o1 = ((c0 + 1) ^ swz) << 4;
-      i32x8 af[C::FB], bf[C::TB];
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) {
-        const char* row = stage + (wf * C::FT + fb * 32 + r_lane) * C::ROW_BYTES;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + o0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + o1);
-        af[fb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+      for (int m = 0; m < NMF; ++m) {
+        const int fb = m / C::TB, tb = m % C::TB;
+        const f32x16 cin = mi == 0 ? f32x16{} : part[fb][tb];
+        // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
+        part[fb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi][fb], bf[mi][tb], cin, 0, 0, 0, 127, 0, 127);
+        if (mi == 0) {
 #pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        const char* row = stage + C::A_BYTES + (wt * C::TT + tb * 32 + r_lane) * C::ROW_BYTES;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + o0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + o1);
-        bf[tb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb)
-#pragma unroll
-        for (int tb = 0; tb < C::TB; ++tb) {
-          const f32x16 cin = mi == 0 ? f32x16{} : part[fb][tb];
-          // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
-          part[fb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fb], bf[tb], cin, 0, 0, 0, 127, 0, 127);
+          for (int q = 0; q < NL; ++q)
+            if ((q < NMF ? q : NMF - 1) == m) load_frag(stage, 1, q, wf, wt, af[1], bf[1]);
         }
+        if (issue) {
+#pragma unroll
+          for (int i = 0; i < C::NI; ++i)
+            if (C::issue_slot(i) == mi * NMF + m) issue_one<COH>(i, kt_next, slot);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
 #pragma unroll
     for (int tb = 0; tb < C::TB; ++tb) {
-      const int q = wt * C::TT + tb * 32 + r_lane;
-      const float st = sx[(q >> 5) * 64 + (q & 31)];
+      const float st = sx[wt * C::TT + tb * 32 + r_lane];
 #pragma unroll
       for (int fb = 0; fb < C::FB; ++fb) {
         const int sel = l1 ? (fb & 1) : ((wf * C::FT + fb * 32) >> 7);
@@ -141,8 +166,11 @@ struct Tile8 {
     }
   }
 
-  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, bool coherent,
-                                           const float* sw, bool l1) {
+  // K loop over nk 128-wide blocks through the NS-stage ring: stage kt is
+  // awaited (own copies, then one workgroup barrier), then multiplied while
+  // the copy of stage kt+NS-1 goes into the slot stage kt-1 used
+  template <bool COH>
+  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, const float* sw, bool l1) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
@@ -150,15 +178,18 @@ struct Tile8 {
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
-      if (s < nk) issue(s, s, coherent);
+      if (s < nk) {
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, s, ring + s * C::STAGE_BYTES);
+      }
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      // the copy of stage kt+NS-1 goes out before waiting for stage kt
-      if (kt > 0) lds_barrier();   // every wavefront is done with stage kt-1
-      if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1, slot == 0 ? C::NS - 1 : slot - 1, coherent);
-      vm_wait_ahead<C::NI, C::NS - 1>(min(C::NS - 1, nk - 1 - kt));
-      lds_barrier();               // stage kt has landed for every wavefront
-      compute(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1);
+      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+      lds_barrier();
+      const int nxt = kt + C::NS - 1;
+      const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
+      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, nxt < nk, nxt,
+                   ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
   }
@@ -174,13 +205,13 @@ struct Meta8 {
   Meta m;
   const char* xs[MOE_MAX_SLICES];
   float wsc[2 * kMaxKBlocks];
-  float amax[4][8][32];   // [wavefront][token block][lane]
 };
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
   __shared__ Meta8 meta8;
+  __shared__ float amax_s[C::NW][C::TB][32];   // per-token h amax: [wavefront][token block][lane]
   Meta& meta = meta8.m;
 
   const int tid = threadIdx.x;
@@ -301,7 +332,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I; },
                  [&](int q) { return hsb + ((size_t)p * C::TM + q) * IB * 4; });
     }
-    tile.mainloop(lds, nk, wf, wt, MOE_H_COHERENT && !l1, meta8.wsc, l1);
+    if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt, meta8.wsc, l1);
+    else tile.template mainloop<true>(lds, nk, wf, wt, meta8.wsc, l1);
     if (rec) {
       rec[4] = (uint32_t)wall_clock64();
       rec[7] = (uint32_t)__builtin_readcyclecounter();
@@ -322,7 +354,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
             mx = fmaxf(mx, fabsf(h));
           }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (lane < 32) meta8.amax[wave][tb][lane] = mx;
+        if (lane < 32) amax_s[wave][tb][lane] = mx;
       }
       __syncthreads();
       char* hwb = static_cast<char*>(a.h);
@@ -331,7 +363,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       for (int tb = 0; tb < C::TB; ++tb) {
         float mx = 0.f;
 #pragma unroll
-        for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, meta8.amax[wt * C::WF + f][tb][lane & 31]);
+        for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, amax_s[wt * C::WF + f][tb][lane & 31]);
         const float scale = mx > 0.f ? mx / 448.f : 1.f;
         const float inv = mx > 0.f ? 448.f / mx : 1.f;
         const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
@@ -406,6 +438,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
 
 // Cfg8<tokens, features, token waves, feature waves, ring stages>
 using Cfg8Main = Cfg8<128, 256, 2, 2, 3>;   // 128 features x 64 tokens per wavefront
+using Cfg8W8 = Cfg8<128, 256, 2, 4, 3>;     // 64 x 64 per wavefront, two wavefronts per SIMD
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -423,6 +456,7 @@ hipError_t occupancy(int* n) {
 extern const TileInfo kFp8Tiles[];
 extern const int kNumFp8Tiles;
 const TileInfo kFp8Tiles[] = {
+    {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},   // first fitting tile is the default
     {21, MOE_FP8_E4M3, Cfg8Main::TM, Cfg8Main::TN, Cfg8Main::THREADS},
 };
 const int kNumFp8Tiles = sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0]);
@@ -430,6 +464,7 @@ const int kNumFp8Tiles = sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0]);
 hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
   switch (id) {
     case 21: return launch<Cfg8Main>(a, s);
+    case 22: return launch<Cfg8W8>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -437,6 +472,7 @@ hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
 hipError_t occupancy_ffn_fp8(int id, int* n) {
   switch (id) {
     case 21: return occupancy<Cfg8Main>(n);
+    case 22: return occupancy<Cfg8W8>(n);
   }
   return hipErrorInvalidValue;
 }

@@ -250,15 +250,19 @@ def test_h_handoff_across_calls_with_poisoned_workspace(tile):
 TOL_FP8 = 5e-2
 
 
+FP8_TILES = [21, 22]
+
+
+@pytest.mark.parametrize("tile", FP8_TILES)
 @pytest.mark.parametrize("H,I,T,L,k,E", [(256, 128, 32, 4, 2, 32), (512, 384, 100, 6, 4, 12),
                                           (1024, 512, 96, 8, 4, 24), (768, 1280, 300, 3, 1, 3)])
-def test_fp8_block_scaled_both_schedules(H, I, T, L, k, E):
+def test_fp8_block_scaled_both_schedules(H, I, T, L, k, E, tile):
     wl = _small_wl(hidden=H, inter=I, tokens_per_slice=T, num_local=L, top_k=k, num_experts=E,
                    dtype="fp8", seed=8000 + H + I + T)
     inp = mi.make_inputs(wl)
     ref = mo.run(inp, block_m=16)
     up = Uploaded(inp)
-    ffn = make_ffn(wl)
+    ffn = make_ffn(wl, tile=tile)
     print(f"[ffn] fp8 H={H} I={I} T={T} tile={ffn.plan.tile}", flush=True)
     _route_and_layout(ffn, up)
     outs = {}
