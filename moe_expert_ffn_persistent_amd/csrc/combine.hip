@@ -20,19 +20,23 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
-  __shared__ int s_cnt[3];
+  __shared__ int s_cnt[4];   // unwritten, clobbered, nonfinite flags; [3]: local-slot mask
   const int n = blockIdx.x;
   const int s = n / a.T;
   const int t = n - s * a.T;
   const bool audit = a.report != nullptr;
-  if (threadIdx.x < 3) s_cnt[threadIdx.x] = 0;
+  if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
   __syncthreads();
+  if (threadIdx.x < a.k && a.pair_row[(size_t)n * a.k + threadIdx.x] >= 0)
+    atomicOr(&s_cnt[3], 1 << threadIdx.x);
+  __syncthreads();
+  const int local_mask = s_cnt[3];
   int unwritten = 0, clobbered = 0, nonfinite = 0;
   const char* base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
   for (int c = threadIdx.x; c < a.H / 8; c += kThreads) {
     float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < a.k; ++j) {
-      const bool local = a.pair_row[(size_t)n * a.k + j] >= 0;
+      const bool local = (local_mask >> j) & 1;
       if (!local && !audit) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(base + ((size_t)j * a.H + c * 8) * 2);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -51,10 +55,11 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
         }
       }
     }
-    if (a.y) {
-      float4* dst = reinterpret_cast<float4*>(a.y + (size_t)n * a.H + c * 8);
-      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
-      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    if (a.y) {   // streamed out: not re-read here
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x4* dst = reinterpret_cast<f32x4*>(a.y + (size_t)n * a.H + c * 8);
+      __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, dst);
+      __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, dst + 1);
     }
   }
   if (audit) {

@@ -56,9 +56,10 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-constexpr int kMaxPerLane = 16;   // E <= 1024
-
+// PER: logits per lane (E <= 64 * PER); instantiated for PER = 1, 2, 4, 8, 16
+template <int PER>
 __global__ void __launch_bounds__(256) route_topk(LayoutArgs a) {
+  constexpr int kMaxPerLane = PER;
   const int lane = threadIdx.x & (kWave - 1);
   const int n = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (n >= a.N) return;
@@ -131,22 +132,41 @@ __global__ void __launch_bounds__(kWave) layout_count(LayoutArgs a) {
   for (int e = lane; e < a.L; e += kWave) a.block_counts[(size_t)blockIdx.x * a.L + e] = s_cnt[e];
 }
 
-__global__ void __launch_bounds__(256) layout_scan(LayoutArgs a) {
-  extern __shared__ int s_tot[];   // [L] per-expert totals
+constexpr int kScanLds = 8192;   // ints of block counts staged in LDS per pass
+
+// Exclusive scan of every expert's column of block_counts over the chunks,
+// then the per-expert totals, row and tile offsets. The counts pass through
+// LDS in row batches (coalesced global traffic; rows padded to L+1 ints so a
+// column read hits distinct banks); one wavefront scans one column at a time.
+__global__ void __launch_bounds__(1024) layout_scan(LayoutArgs a) {
+  extern __shared__ int s_tot[];   // [L] running per-expert totals, then the staging rows
+  int* s_buf = s_tot + a.L;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
-  // 1) per expert: exclusive scan over chunks, in place
-  for (int e = wave; e < a.L; e += nwaves) {
-    int carry = 0;
-    for (int c0 = 0; c0 < a.nchunks; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = c < a.nchunks ? a.block_counts[(size_t)c * a.L + e] : 0;
-      const int inc = wave_inclusive_scan(v);
-      if (c < a.nchunks) a.block_counts[(size_t)c * a.L + e] = carry + inc - v;
-      carry += __shfl(inc, kWave - 1, kWave);
+  const int L = a.L, LP = a.L + 1;
+  const int rows_per_pass = kScanLds / LP;
+  for (int e = threadIdx.x; e < L; e += blockDim.x) s_tot[e] = 0;
+  for (int c0 = 0; c0 < a.nchunks; c0 += rows_per_pass) {
+    const int nr = min(rows_per_pass, a.nchunks - c0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * L; i += blockDim.x)
+      s_buf[(i / L) * LP + i % L] = a.block_counts[(size_t)c0 * L + i];
+    __syncthreads();
+    for (int e = wave; e < L; e += nwaves) {
+      int carry = s_tot[e];
+      for (int r0 = 0; r0 < nr; r0 += kWave) {
+        const int r = r0 + lane;
+        const int v = r < nr ? s_buf[r * LP + e] : 0;
+        const int inc = wave_inclusive_scan(v);
+        if (r < nr) s_buf[r * LP + e] = carry + inc - v;
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
+      if (lane == 0) s_tot[e] = carry;
     }
-    if (lane == 0) s_tot[e] = carry;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * L; i += blockDim.x)
+      a.block_counts[(size_t)c0 * L + i] = s_buf[(i / L) * LP + i % L];
   }
   __syncthreads();
   // 2) over experts: row offsets, scheduler-row offsets, totals
@@ -189,11 +209,21 @@ __global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
   const int f0 = blockIdx.x * kLayoutChunk;
   const int f1 = min(total, f0 + kLayoutChunk);
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int fb = f0; fb < f1; fb += kWave) {
-    const int f = fb + lane;
+  constexpr int kSub = kLayoutChunk / kWave;
+  int ge[kSub];     // the chunk's expert ids and weights, loaded before any placement
+  float gw[kSub];
+#pragma unroll
+  for (int i = 0; i < kSub; ++i) {
+    const int f = f0 + i * kWave + lane;
+    ge[i] = f < f1 ? a.topk_idx[f] - a.e0 : -1;
+    gw[i] = f < f1 ? a.topk_w[f] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kSub; ++i) {
+    const int f = f0 + i * kWave + lane;
     int e = -1;
     if (f < f1) {
-      const int g = a.topk_idx[f] - a.e0;
+      const int g = ge[i];
       if (g >= 0 && g < a.L) e = g;
       else a.pair_row[f] = -1;
     }
@@ -206,7 +236,7 @@ __global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
       if (e == le) {
         const int r = base + __popcll(same & below);
         a.row_pair[r] = f;
-        a.row_weight[r] = a.topk_w[f];
+        a.row_weight[r] = gw[i];
         a.pair_row[f] = r;
       }
       __syncthreads();
@@ -222,11 +252,16 @@ __global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (a.logits && a.N > 0) {
     const int per_block = 4;   // tokens (wavefronts) per workgroup
-    route_topk<<<(a.N + per_block - 1) / per_block, per_block * kWave, 0, stream>>>(a);
+    const dim3 grid((a.N + per_block - 1) / per_block), block(per_block * kWave);
+    if (a.E <= 64) route_topk<1><<<grid, block, 0, stream>>>(a);
+    else if (a.E <= 128) route_topk<2><<<grid, block, 0, stream>>>(a);
+    else if (a.E <= 256) route_topk<4><<<grid, block, 0, stream>>>(a);
+    else if (a.E <= 512) route_topk<8><<<grid, block, 0, stream>>>(a);
+    else route_topk<16><<<grid, block, 0, stream>>>(a);
   }
   const size_t lds = sizeof(int) * (size_t)a.L;
   if (a.nchunks > 0) layout_count<<<a.nchunks, kWave, lds, stream>>>(a);
-  layout_scan<<<1, 256, lds, stream>>>(a);
+  layout_scan<<<1, 1024, lds + sizeof(int) * kScanLds, stream>>>(a);
   if (a.nchunks > 0) layout_place<<<a.nchunks, kWave, lds, stream>>>(a);
   return hipGetLastError();
 }
