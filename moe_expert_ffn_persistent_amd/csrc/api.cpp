@@ -8,6 +8,10 @@
 
 #include "internal.hpp"
 
+#ifndef MOE_XCD_BY_NTILE
+#define MOE_XCD_BY_NTILE -1   // -1: automatic, 0: never, 1: whenever the grid allows
+#endif
+
 namespace moe {
 
 extern const TileInfo kBf16Tiles[];
@@ -279,6 +283,15 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   a.N1 = plan.n1_tiles;
   a.N2 = plan.n2_tiles;
   a.grid = plan.grid;
+  // Group logical ids by Linear-1 N-tile per XCD when the experts span
+  // several M-blocks (their weight tiles are then read once per XCD instead
+  // of once per M-block); otherwise keep a row's N-tiles on one XCD.
+  {
+    const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
+    const bool fits = a.grid % 8 == 0 && a.N1 % 8 == 0 && a.grid % a.N1 == 0;
+    const bool want = MOE_XCD_BY_NTILE > 0 || (MOE_XCD_BY_NTILE < 0 && avg >= 2.0 * plan.block_m);
+    a.xcd_group = fits && want ? a.N1 / 8 : 0;
+  }
   a.schedule = prm->schedule;
   a.lead_d = plan.lead_d;
   a.experts_per_wave = prm->experts_per_wave;

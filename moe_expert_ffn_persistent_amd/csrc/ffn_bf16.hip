@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   // XCDs, so consecutive logical ids are placed on the same XCD (and share
   // its L2) when the grid is a multiple of 8
   const int G = a.grid;
-  const int g = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int g = logical_instance(G, a.xcd_group);
 
   InterleavedStream ist;
   ExpertWaveStream ews;

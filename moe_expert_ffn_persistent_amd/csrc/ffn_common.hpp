@@ -49,6 +49,21 @@ enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
 #define MOE_H_COHERENT 1
 #endif
 
+// Logical instance id of this workgroup. Workgroups are dispatched
+// round-robin over the 8 XCDs (block b runs on XCD b mod 8), each with its
+// own L2. By default consecutive logical ids share an XCD, so the N-tiles of
+// one row (which read the same token rows) meet in one L2. With xcd_group R,
+// XCD x holds the ids with g mod N1 in [xR, xR+R): when N1 divides the grid,
+// an instance's Linear-1 tiles all have N-tile g mod N1, so the M-blocks of
+// one expert that read the same weight tile meet in one L2.
+__device__ __forceinline__ int logical_instance(int G, int xcd_group) {
+  const int b = (int)blockIdx.x;
+  if (G % 8 != 0) return b;
+  const int x = b % 8, i = b / 8;
+  if (xcd_group > 0) return (i / xcd_group) * (8 * xcd_group) + x * xcd_group + i % xcd_group;
+  return x * (G / 8) + i;
+}
+
 // One 1 KiB global->LDS copy for the wavefront: lane l's 16 bytes from src
 // land at LDS byte address m0 + 16*l. Issued from inline assembly so the
 // compiler does not serialise later LDS reads behind it; completion is

@@ -45,6 +45,8 @@ struct Cfg8 {
   static constexpr int SCALE_OFF = (TN + TM) * ROW_BYTES;
   static constexpr int STAGE_BYTES = SCALE_OFF + NW * 256;
   static constexpr int NM = 2 * FB * TB;                // MFMAs per wavefront per stage
+  // MFMA of the first step after which the second step's fragments are read
+  static constexpr int FRAG1_AFTER = NW >= 8 ? FB * TB - 1 : 0;
   // copy i of a stage is issued after MFMA issue_slot(i) of the stage before
   static constexpr int issue_slot(int i) { return i * NM * MOE_ISSUE_SPREAD / (NI * 8); }
   static_assert(TN == 256, "an N-tile must own exactly one 128-column h-scale block");
@@ -62,6 +64,8 @@ struct Tile8 {
   const char* src[C::NID];
   const char* ssrc;          // this lane's token-scale source for stage 0
   f32x16 acc[C::FB][C::TB];
+  f32x16 part[C::FB][C::TB];   // partial tile of the current K block
+  float st_prev[C::TB];        // token scales of the previous K block (lagging wavefronts)
   uint32_t ring;
 
   template <class WRow, class TRow, class SRow>
@@ -115,21 +119,38 @@ struct Tile8 {
     else bf[q - C::FB] = v;
   }
 
-  // one 128-wide K block: two MFMAs per output block into a partial tile
+  // acc += part * (token scale x weight scale of K block kb), per output block
+  __device__ __forceinline__ void promote(const float (&st)[C::TB], int kb, int wf, const float* sw,
+                                          bool l1) {
+#pragma unroll
+    for (int tb = 0; tb < C::TB; ++tb)
+#pragma unroll
+      for (int fb = 0; fb < C::FB; ++fb) {
+        const int sel = l1 ? (fb & 1) : ((wf * C::FT + fb * 32) >> 7);
+        const float s = st[tb] * sw[sel * kMaxKBlocks + kb];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[fb][tb][v] += part[fb][tb][v] * s;
+      }
+  }
+
+  // One 128-wide K block: two MFMAs per output block into the partial tile
   // (the copy of a later stage spread between them, fragments of the second
-  // step read during the first), then promotion with the block's token and
-  // weight scales (sw: LDS, [2][kMaxKBlocks])
+  // step read during the first), and the promotion with the block's token
+  // and weight scales (sw: LDS, [2][kMaxKBlocks]). `lag` wavefronts promote
+  // a stage's partial at the start of the next stage instead of at its end:
+  // the two wavefronts sharing a SIMD then alternate between MFMAs and VALU
+  // promotion after every workgroup barrier rather than promoting together.
   template <bool COH>
   __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
-                                          bool l1, bool issue, int kt_next, uint32_t slot) {
+                                          bool l1, bool lag, bool issue, int kt_next, uint32_t slot) {
     constexpr int NMF = C::FB * C::TB;
     constexpr int NL = C::FB + C::TB;
     const int lane = threadIdx.x & 63;
     const int r_lane = lane & 31;
     i32x8 af[2][C::FB], bf[2][C::TB];
-    f32x16 part[C::FB][C::TB];
 #pragma unroll
     for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
+    if (lag && kt > 0) promote(st_prev, kt - 1, wf, sw, l1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -139,10 +160,11 @@ struct Tile8 {
         const f32x16 cin = mi == 0 ? f32x16{} : part[fb][tb];
         // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
         part[fb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi][fb], bf[mi][tb], cin, 0, 0, 0, 127, 0, 127);
-        if (mi == 0) {
+        if (mi == 0 && m == C::FRAG1_AFTER) {
+          // the second step's fragments (after the last first-step MFMA with
+          // eight wavefronts, so that the two fragment sets share registers)
 #pragma unroll
-          for (int q = 0; q < NL; ++q)
-            if ((q < NMF ? q : NMF - 1) == m) load_frag(stage, 1, q, wf, wt, af[1], bf[1]);
+          for (int q = 0; q < NL; ++q) load_frag(stage, 1, q, wf, wt, af[1], bf[1]);
         }
         if (issue) {
 #pragma unroll
@@ -152,29 +174,32 @@ struct Tile8 {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // this stage's token scales; a lagging wavefront keeps them for the next
+    // stage (the slot is refilled only by a copy issued during the next stage)
     const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
+    float st[C::TB];
 #pragma unroll
-    for (int tb = 0; tb < C::TB; ++tb) {
-      const float st = sx[wt * C::TT + tb * 32 + r_lane];
+    for (int tb = 0; tb < C::TB; ++tb) st[tb] = sx[wt * C::TT + tb * 32 + r_lane];
+    if (lag) {
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) {
-        const int sel = l1 ? (fb & 1) : ((wf * C::FT + fb * 32) >> 7);
-        const float s = st * sw[sel * kMaxKBlocks + kt];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[fb][tb][v] += part[fb][tb][v] * s;
-      }
+      for (int tb = 0; tb < C::TB; ++tb) st_prev[tb] = st[tb];
+    } else {
+      promote(st, kt, wf, sw, l1);
     }
   }
 
   // K loop over nk 128-wide blocks through the NS-stage ring: stage kt is
   // awaited (own copies, then one workgroup barrier), then multiplied while
-  // the copy of stage kt+NS-1 goes into the slot stage kt-1 used
+  // the copy of stage kt+NS-1 goes into the slot stage kt-1 used. With eight
+  // wavefronts the second half (on the same SIMDs as the first half) promotes
+  // one stage late.
   template <bool COH>
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, const float* sw, bool l1) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) acc[fb][tb] = f32x16{};
+    const bool lag = C::NW >= 8 && (int)(threadIdx.x >> 6) >= C::NW / 2;
     lds_barrier();
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
@@ -188,10 +213,11 @@ struct Tile8 {
       lds_barrier();
       const int nxt = kt + C::NS - 1;
       const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, nxt < nk, nxt,
+      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, lag, nxt < nk, nxt,
                    ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
+    if (lag && nk > 0) promote(st_prev, nk - 1, wf, sw, l1);
   }
 };
 
@@ -234,7 +260,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   __syncthreads();
   const int P = uni(meta.tile_off[L]);
   const int G = a.grid;
-  const int g = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int g = logical_instance(G, a.xcd_group);
 
   InterleavedStream ist;
   ExpertWaveStream ews;

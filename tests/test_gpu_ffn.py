@@ -137,6 +137,43 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
         assert (np.diff(st, axis=1) >= 0).all() or (st.max() - st.min() > 2 ** 31)
 
 
+@pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
+def test_xcd_placement_by_ntile_changes_nothing_but_placement(schedule):
+    # tile 3 (32 x 128) with I = 1024 gives N1 = 16 Linear-1 N-tiles and
+    # experts of ~128 rows (>= 2 M-blocks): with grid 32 (a multiple of N1)
+    # the host groups logical ids by N-tile per XCD, with grid 24 it keeps
+    # consecutive ids; streams, oracle parity and output bits are unchanged
+    wl = _small_wl(tokens_per_slice=64, num_experts=8, top_k=2, num_local=4, hidden=256,
+                   inter=1024, seed=4242)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=32)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl, tile=3)
+    _route_and_layout(ffn, up)
+    tile_offset = ffn.layout_bufs.tile_offset.cpu().numpy().tolist()
+    bits = {}
+    for grid in (32, 24):
+        plan = ffn.resolved_plan(grid=grid)
+        assert plan.n1_tiles == 16
+        cap = 2048
+        trace = torch.full((grid, cap, 8), -1, dtype=torch.int32, device=dev())
+        print(f"[ffn] xcd placement {schedule} grid={grid}", flush=True)
+        up.reset_combine()
+        ffn.forward(up.x_slices, up.w1, up.w2, up.comb_slices, schedule=schedule, grid=grid,
+                    trace=trace, trace_capacity=cap)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        _check_against_oracle(up, ref)
+        want = sc.all_streams(schedule, grid, tile_offset, plan.n1_tiles, plan.n2_tiles,
+                              plan.lead_d, 0)
+        tr = trace.cpu().numpy()
+        for g in range(grid):
+            used = tr[g][tr[g][:, 0] != -1]
+            assert [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used] == want[g]
+        bits[grid] = up.combine_bits().copy()
+    assert (bits[32] == bits[24]).all()
+
+
 def test_watchdog_reports_timeout_instead_of_hanging():
     wl = mi.get_workload("tiny")
     inp = mi.make_inputs(wl)
