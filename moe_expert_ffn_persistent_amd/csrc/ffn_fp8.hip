@@ -4,11 +4,15 @@
 // evaluation, section 5.1, ran W8A8). Same task structure and schedules as
 // the bf16 kernel (ffn_bf16.hip); what differs:
 //
-//  - MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with unit (2^0) MX scales: the
-//    fp32 block scales are not powers of two, so they cannot ride in the MFMA.
-//    Each stage covers exactly one 128-wide K block: its two MFMAs accumulate
-//    into a partial tile, which the VALU then adds into the fp32 accumulator
-//    times (token scale x weight scale) of that block.
+//  - MFMA with unit (2^0) MX scales: the fp32 block scales are not powers
+//    of two, so they cannot ride in the MFMA. Each stage covers exactly one
+//    128-wide K block. Tile8: two v_mfma_scale_f32_32x32x64_f8f6f4 per 32x32
+//    output block accumulate a partial tile, which the VALU then adds into
+//    the fp32 accumulator times (token scale x weight scale) of that block.
+//    Tile8W: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 block covers
+//    the whole K block, and each block is promoted right behind the matrix
+//    core, which keeps the register budget of a 192 x 256 tile within eight
+//    wavefronts (fewer copy bytes per FLOP than 128 x 256).
 //  - Token scales of the stage are copied into LDS next to the operands by
 //    four-byte direct-to-LDS copies; the weight scales of the task (two
 //    128-row blocks) are staged in LDS once per task.
@@ -27,9 +31,12 @@
 namespace moe {
 namespace {
 
-template <int TM_, int TN_, int WT_, int WF_, int NS_>
+template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false>
 struct Cfg8 {
   static constexpr int TM = TM_, TN = TN_, WT = WT_, WF = WF_, NS = NS_;
+  // WIDE: 16x16x128 MFMAs (one per output block and K block), promoted
+  // block by block between them (Tile8W); else 32x32x64 MFMAs (Tile8)
+  static constexpr bool WIDE = WIDE_;
   static constexpr int NW = WT * WF;
   static constexpr int THREADS = 64 * NW;
   static constexpr int TT = TM / WT, FT = TN / WF;
@@ -44,7 +51,9 @@ struct Cfg8 {
   // into its own 256-byte slot, so row q's scale sits at word q
   static constexpr int SCALE_OFF = (TN + TM) * ROW_BYTES;
   static constexpr int STAGE_BYTES = SCALE_OFF + NW * 256;
-  static constexpr int NM = 2 * FB * TB;                // MFMAs per wavefront per stage
+  // MFMAs per wavefront per stage: one 16x16x128 per 16 x 16 block (WIDE), or
+  // two 32x32x64 per 32 x 32 block
+  static constexpr int NM = WIDE ? (FT / 16) * (TT / 16) : 2 * FB * TB;
   // MFMA of the first step after which the second step's fragments are read
   static constexpr int FRAG1_AFTER = NW >= 8 ? FB * TB - 1 : 0;
   // copy i of a stage is issued after MFMA issue_slot(i) of the stage before
@@ -59,13 +68,25 @@ struct Cfg8 {
 
 constexpr int kMaxKBlocks = 128;   // H/128 and I/128 limit
 
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// e4m3 code of clamp(h * inv, +-448) for four values, round to nearest even
+__device__ __forceinline__ uint32_t quant4(const float (&h)[4], float inv) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[i] * inv, -448.f), 448.f);
+  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
+}
+
+// Operand and token-scale copies, shared by both fp8 tiles.
 template <class C>
-struct Tile8 {
+struct Tile8Copies {
   const char* src[C::NID];
   const char* ssrc;          // this lane's token-scale source for stage 0
-  f32x16 acc[C::FB][C::TB];
-  f32x16 part[C::FB][C::TB];   // partial tile of the current K block
-  float st_prev[C::TB];        // token scales of the previous K block (lagging wavefronts)
   uint32_t ring;
 
   template <class WRow, class TRow, class SRow>
@@ -101,22 +122,63 @@ struct Tile8 {
     }
   }
 
+  // 32 bytes of 128-byte row r of the stage at logical 16-byte chunks c, c+1
+  __device__ __forceinline__ static i32x8 frag32(const char* stage, int r, int c) {
+    const int swz = (r >> 1) & 7;
+    const char* row = stage + r * C::ROW_BYTES;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c ^ swz) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c + 1) ^ swz) << 4));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+
+  // K loop over nk 128-wide blocks through the NS-stage ring: stage kt is
+  // awaited (own copies, then one workgroup barrier), then multiplied (by the
+  // tile's compute) while the copy of stage kt+NS-1 goes into the slot stage
+  // kt-1 used. The copy is issued unconditionally (the last NS-1 stages
+  // re-copy stage nk-1 into their free slot), so no branch splits the MFMA
+  // sequence it is spread over; those extra copies are awaited at the end,
+  // before the epilogue reuses LDS.
+  template <bool COH, class Tile>
+  __device__ __forceinline__ void kloop(Tile& t, char* lds, int nk, int wf, int wt, const float* sw,
+                                        bool l1) {
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s) {
+      const int ks = min(s, nk - 1);
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, ks, ring + s * C::STAGE_BYTES);
+    }
+    int slot = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<C::NI * (C::NS - 2)>();   // stage kt has landed (later stages may not have)
+      lds_barrier();
+      const int nxt = min(kt + C::NS - 1, nk - 1);
+      const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
+      t.template compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, nxt,
+                              ring + nslot * C::STAGE_BYTES);
+      slot = slot + 1 == C::NS ? 0 : slot + 1;
+    }
+    vm_wait<0>();
+  }
+};
+
+// 32x32x64 MFMAs: lane l of an output block holds token column l%32 and
+// feature rows 8*(v/4) + 4*(l/32) + v%4.
+template <class C>
+struct Tile8 : Tile8Copies<C> {
+  f32x16 acc[C::FB][C::TB];
+  f32x16 part[C::FB][C::TB];   // partial tile of the current K block
+  float st_prev[C::TB];        // token scales of the previous K block (lagging wavefronts)
+  bool lag;
+
   // fragment q (q < FB: weights, else tokens) of MFMA step mi: 32 K-elements
-  // per lane from two swizzled 16-byte chunks
+  // per lane
   __device__ __forceinline__ void load_frag(const char* stage, int mi, int q, int wf, int wt,
                                             i32x8 (&af)[C::FB], i32x8 (&bf)[C::TB]) {
     const int lane = threadIdx.x & 63;
-    const int r_lane = lane & 31;
-    const int swz = (r_lane >> 1) & 7;
     const int c0 = 4 * mi + 2 * (lane >> 5);
-    const int o0 = (c0 ^ swz) << 4, o1 = ((c0 + 1) ^ swz) << 4;
-    const char* row = q < C::FB ? stage + (wf * C::FT + q * 32 + r_lane) * C::ROW_BYTES
-                                : stage + C::A_BYTES + (wt * C::TT + (q - C::FB) * 32 + r_lane) * C::ROW_BYTES;
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + o0);
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + o1);
-    const i32x8 v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    if (q < C::FB) af[q] = v;
-    else bf[q - C::FB] = v;
+    if (q < C::FB) af[q] = this->frag32(stage, wf * C::FT + q * 32 + (lane & 31), c0);
+    else bf[q - C::FB] = this->frag32(stage, C::TN + wt * C::TT + (q - C::FB) * 32 + (lane & 31), c0);
   }
 
   // acc += part * (token scale x weight scale of K block kb), per output block
@@ -134,19 +196,18 @@ struct Tile8 {
   }
 
   // One 128-wide K block: two MFMAs per output block into the partial tile
-  // (the copy of a later stage spread between them, fragments of the second
-  // step read during the first), and the promotion with the block's token
-  // and weight scales (sw: LDS, [2][kMaxKBlocks]). `lag` wavefronts promote
-  // a stage's partial at the start of the next stage instead of at its end:
-  // the two wavefronts sharing a SIMD then alternate between MFMAs and VALU
-  // promotion after every workgroup barrier rather than promoting together.
+  // (the copy of a later stage spread between them), and the promotion with
+  // the block's token and weight scales (sw: LDS, [2][kMaxKBlocks]). `lag`
+  // wavefronts promote a stage's partial at the start of the next stage
+  // instead of at its end: the two wavefronts sharing a SIMD then alternate
+  // between MFMAs and VALU promotion after every workgroup barrier rather
+  // than promoting together.
   template <bool COH>
   __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
-                                          bool l1, bool lag, bool issue, int kt_next, uint32_t slot) {
+                                          bool l1, int kt_next, uint32_t slot) {
     constexpr int NMF = C::FB * C::TB;
     constexpr int NL = C::FB + C::TB;
-    const int lane = threadIdx.x & 63;
-    const int r_lane = lane & 31;
+    const int r_lane = threadIdx.x & 31;
     i32x8 af[2][C::FB], bf[2][C::TB];
 #pragma unroll
     for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
@@ -166,11 +227,9 @@ struct Tile8 {
 #pragma unroll
           for (int q = 0; q < NL; ++q) load_frag(stage, 1, q, wf, wt, af[1], bf[1]);
         }
-        if (issue) {
 #pragma unroll
-          for (int i = 0; i < C::NI; ++i)
-            if (C::issue_slot(i) == mi * NMF + m) issue_one<COH>(i, kt_next, slot);
-        }
+        for (int i = 0; i < C::NI; ++i)
+          if (C::issue_slot(i) == mi * NMF + m) this->template issue_one<COH>(i, kt_next, slot);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -188,44 +247,258 @@ struct Tile8 {
     }
   }
 
-  // K loop over nk 128-wide blocks through the NS-stage ring: stage kt is
-  // awaited (own copies, then one workgroup barrier), then multiplied while
-  // the copy of stage kt+NS-1 goes into the slot stage kt-1 used. With eight
-  // wavefronts the second half (on the same SIMDs as the first half) promotes
-  // one stage late.
+  // With eight wavefronts the second half (on the same SIMDs as the first
+  // half) promotes one stage late.
   template <bool COH>
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, const float* sw, bool l1) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) acc[fb][tb] = f32x16{};
-    const bool lag = C::NW >= 8 && (int)(threadIdx.x >> 6) >= C::NW / 2;
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s)
-      if (s < nk) {
-#pragma unroll
-        for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, s, ring + s * C::STAGE_BYTES);
-      }
-    int slot = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
-      lds_barrier();
-      const int nxt = kt + C::NS - 1;
-      const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, lag, nxt < nk, nxt,
-                   ring + nslot * C::STAGE_BYTES);
-      slot = slot + 1 == C::NS ? 0 : slot + 1;
-    }
+    lag = C::NW >= 8 && (int)(threadIdx.x >> 6) >= C::NW / 2;
+    this->template kloop<COH>(*this, lds, nk, wf, wt, sw, l1);
     if (lag && nk > 0) promote(st_prev, nk - 1, wf, sw, l1);
+  }
+
+  // Linear-1: SwiGLU, per-token amax over the N-tile's 128 h columns
+  // (within the lane, across the lane pair l, l+32, then across the feature
+  // wavefronts through LDS), e4m3 h and its scale
+  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wf = wave % C::WF, wt = wave / C::WF;
+    float hv[C::TB][C::FB / 2][16];
+#pragma unroll
+    for (int tb = 0; tb < C::TB; ++tb) {
+      float mx = 0.f;
+#pragma unroll
+      for (int fp = 0; fp < C::FB / 2; ++fp)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float h = silu(acc[2 * fp][tb][v]) * acc[2 * fp + 1][tb][v];
+          hv[tb][fp][v] = h;
+          mx = fmaxf(mx, fabsf(h));
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (lane < 32) amax[wave * C::TT + tb * 32 + lane] = mx;
+    }
+    __syncthreads();
+    char* hwb = static_cast<char*>(a.h);
+    const int IB = a.I / 128;
+#pragma unroll
+    for (int tb = 0; tb < C::TB; ++tb) {
+      float mx = 0.f;
+#pragma unroll
+      for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, amax[(wt * C::WF + f) * C::TT + tb * 32 + (lane & 31)]);
+      const float scale = mx > 0.f ? mx / 448.f : 1.f;
+      const float inv = mx > 0.f ? 448.f / mx : 1.f;
+      const size_t hrow = (size_t)p * C::TM + wt * C::TT + tb * 32 + (lane & 31);
+      char* hr = hwb + hrow * a.I;
+#pragma unroll
+      for (int fp = 0; fp < C::FB / 2; ++fp) {
+        const int col0 = j0 + (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float h4[4] = {hv[tb][fp][g4 * 4], hv[tb][fp][g4 * 4 + 1], hv[tb][fp][g4 * 4 + 2],
+                               hv[tb][fp][g4 * 4 + 3]};
+          __hip_atomic_store(reinterpret_cast<uint32_t*>(hr + col0 + g4 * 8), quant4(h4, inv),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (wf == 0 && lane < 32)
+        __hip_atomic_store(a.hs + hrow * IB + n, scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // Linear-2: bf16(w * acc) into the combine slot of each routed row
+  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, int r_base,
+                                         char* const* comb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wf = wave % C::WF, wt = wave / C::WF;
+#pragma unroll
+    for (int tb = 0; tb < C::TB; ++tb) {
+      const int mm = m * C::TM + wt * C::TT + tb * 32 + (lane & 31);
+      if (mm < Me) {
+        const int r = r_base + mm;
+        const int f = a.row_pair[r];
+        const float w = a.row_weight[r];
+        const int tok = f / a.k;
+        const int j = f - tok * a.k;
+        const int s = tok / a.T;
+        char* dst = comb[s] + ((size_t)(tok - s * a.T) * a.k + j) * a.H * 2;
+#pragma unroll
+        for (int fb = 0; fb < C::FB; ++fb) {
+          const int col0 = n * C::TN + wf * C::FT + fb * 32 + (lane >> 5) * 4;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x16& v = acc[fb][tb];
+            const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
+                               ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
+            uint64_t* d = reinterpret_cast<uint64_t*>(dst + (size_t)(col0 + g4 * 8) * 2);
+            if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);
+            else *d = o;
+          }
+        }
+      }
+    }
   }
 };
 
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
+// 16x16x128 MFMAs (the whole K block of a stage in one instruction): lane l
+// of an output block holds token column l%16 and feature rows 4*(l/16) + i.
+// Each wavefront keeps its four weight fragments for the stage and streams
+// its token fragments; each block's product is promoted into acc two MFMAs
+// after it was issued (three partial blocks in flight), so the VALU work
+// runs under the matrix core instead of after the stage. With FT = 64 the
+// accumulators take 128 registers, which makes 256 x 256 tiles (half the
+// copy bytes per FLOP of 128 x 256) fit eight wavefronts.
+template <class C>
+struct Tile8W : Tile8Copies<C> {
+  static constexpr int FB16 = C::FT / 16, TB16 = C::TT / 16;
+  static_assert(C::FT == 64, "gate/up pairing assumes one 32-row gate and one 32-row up block per wavefront");
+  static_assert(FB16 >= 2, "a token block's scale is replaced only after two promotion steps");
+  f32x4 acc[FB16][TB16];
+
+  __device__ __forceinline__ float block_scale(const float* sw, int kt, int wf, int i, bool l1) const {
+    const int row = wf * C::FT + i * 16;   // first feature row of block i in the N-tile
+    const int sel = l1 ? ((row >> 5) & 1) : (row >> 7);
+    return sw[sel * kMaxKBlocks + kt];
+  }
+
+  template <bool COH>
+  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
+                                          bool l1, int kt_next, uint32_t slot) {
+    constexpr int NB = FB16 * TB16;   // output blocks = MFMAs per stage
+    const int lane = threadIdx.x & 63;
+    const int r16 = lane & 15, c0 = 2 * (lane >> 4);
+    i32x8 af[FB16], bf[2];
+#pragma unroll
+    for (int i = 0; i < FB16; ++i) af[i] = this->frag32(stage, wf * C::FT + i * 16 + r16, c0);
+    bf[0] = this->frag32(stage, C::TN + wt * C::TT + r16, c0);
+    const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
+    float swv[FB16];
+#pragma unroll
+    for (int i = 0; i < FB16; ++i) swv[i] = block_scale(sw, kt, wf, i, l1);
+    f32x4 part[3];
+    float stj[2];
+    stj[0] = sx[wt * C::TT + r16];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NB + 2; ++b) {
+      const int j = b / FB16, i = b % FB16;   // token block, feature block
+      if (b < NB) {
+        // next token block: its fragment once this block's first MFMA is out,
+        // its scale once the promotions of the block before it are done
+        if (i == 0 && j + 1 < TB16)
+          bf[(j + 1) & 1] = this->frag32(stage, C::TN + wt * C::TT + (j + 1) * 16 + r16, c0);
+        if (i == FB16 / 2 && j + 1 < TB16) stj[(j + 1) & 1] = sx[wt * C::TT + (j + 1) * 16 + r16];
+        // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
+        part[b % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j & 1], f32x4{}, 0, 0, 0, 127,
+                                                                       0, 127);
+      }
+      if (b >= 2) {
+        const int q = b - 2, qj = q / FB16, qi = q % FB16;
+        const float s = stj[qj & 1] * swv[qi];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[qi][qj][v] += part[q % 3][v] * s;
+      }
+#pragma unroll
+      for (int k = 0; k < C::NI; ++k)
+        if (C::issue_slot(k) == b) this->template issue_one<COH>(k, kt_next, slot);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  template <bool COH>
+  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, const float* sw, bool l1) {
+#pragma unroll
+    for (int i = 0; i < FB16; ++i)
+#pragma unroll
+      for (int j = 0; j < TB16; ++j) acc[i][j] = f32x4{};
+    this->template kloop<COH>(*this, lds, nk, wf, wt, sw, l1);
+  }
+
+  // Linear-1: blocks 0-1 of the wavefront are gate rows, 2-3 the matching up
+  // rows (32-row interleave of W1's N-tile); per-token amax over the N-tile's
+  // 128 h columns: within the lane (8 values), across the four lanes of a
+  // token column (l, l^16, l^32, l^48), then across the feature wavefronts
+  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wf = wave % C::WF, wt = wave / C::WF;
+    const int r16 = lane & 15;
+    float hv[TB16][2][4];
+#pragma unroll
+    for (int j = 0; j < TB16; ++j) {
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float h = silu(acc[i][j][v]) * acc[i + 2][j][v];
+          hv[j][i][v] = h;
+          mx = fmaxf(mx, fabsf(h));
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (lane < 16) amax[wave * C::TT + j * 16 + lane] = mx;
+    }
+    __syncthreads();
+    char* hwb = static_cast<char*>(a.h);
+    const int IB = a.I / 128;
+#pragma unroll
+    for (int j = 0; j < TB16; ++j) {
+      float mx = 0.f;
+#pragma unroll
+      for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, amax[(wt * C::WF + f) * C::TT + j * 16 + r16]);
+      const float scale = mx > 0.f ? mx / 448.f : 1.f;
+      const float inv = mx > 0.f ? 448.f / mx : 1.f;
+      const size_t hrow = (size_t)p * C::TM + wt * C::TT + j * 16 + r16;
+      char* hr = hwb + hrow * a.I + j0 + wf * 32 + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(hr + i * 16), quant4(hv[j][i], inv), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (wf == 0 && lane < 16)
+        __hip_atomic_store(a.hs + hrow * IB + n, scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // Linear-2: bf16(w * acc) into the combine slot of each routed row, four
+  // consecutive features (8 bytes) per lane and block
+  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, int r_base,
+                                         char* const* comb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wf = wave % C::WF, wt = wave / C::WF;
+    const int r16 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < TB16; ++j) {
+      const int mm = m * C::TM + wt * C::TT + j * 16 + r16;
+      if (mm < Me) {
+        const int r = r_base + mm;
+        const int f = a.row_pair[r];
+        const float w = a.row_weight[r];
+        const int tok = f / a.k;
+        const int slot = f - tok * a.k;
+        const int s = tok / a.T;
+        char* dst = comb[s] + (((size_t)(tok - s * a.T) * a.k + slot) * a.H + n * C::TN + wf * C::FT +
+                               4 * (lane >> 4)) * 2;
+#pragma unroll
+        for (int i = 0; i < FB16; ++i) {
+          const f32x4& v = acc[i][j];
+          const uint64_t o = (uint64_t)pack_bf16x2(w * v[0], w * v[1]) |
+                             ((uint64_t)pack_bf16x2(w * v[2], w * v[3]) << 32);
+          uint64_t* d = reinterpret_cast<uint64_t*>(dst + i * 32);
+          if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);
+          else *d = o;
+        }
+      }
+    }
+  }
+};
+
+template <class C, bool WIDE = C::WIDE>
+struct TileOf { using type = Tile8<C>; };
+template <class C>
+struct TileOf<C, true> { using type = Tile8W<C>; };
 
 struct Meta8 {
   Meta m;
@@ -237,7 +510,7 @@ template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
   __shared__ Meta8 meta8;
-  __shared__ float amax_s[C::NW][C::TB][32];   // per-token h amax: [wavefront][token block][lane]
+  __shared__ float amax_s[C::NW * C::TT];   // per-token h amax of each wavefront
   Meta& meta = meta8.m;
 
   const int tid = threadIdx.x;
@@ -268,7 +541,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   if (interleaved) ist.init(g, G, P, a.N1, a.N2, a.lead_d);
   else ews.init(g, G, a.N1, a.N2, meta.wave_row, uni(meta.nwaves));
 
-  Tile8<C> tile;
+  typename TileOf<C>::type tile;
   tile.ring = (uint32_t)(uintptr_t)lds;
   int seq = 0;
   for (;;) {
@@ -366,82 +639,15 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
     }
 
     if (l1) {
-      // SwiGLU, per-token amax over the tile's 128 h columns, e4m3 h + scale
-      float hv[C::TB][C::FB / 2][16];
-#pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        float mx = 0.f;
-#pragma unroll
-        for (int fp = 0; fp < C::FB / 2; ++fp)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float h = silu(tile.acc[2 * fp][tb][v]) * tile.acc[2 * fp + 1][tb][v];
-            hv[tb][fp][v] = h;
-            mx = fmaxf(mx, fabsf(h));
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        if (lane < 32) amax_s[wave][tb][lane] = mx;
-      }
-      __syncthreads();
-      char* hwb = static_cast<char*>(a.h);
-      float* hsw = a.hs;
-#pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        float mx = 0.f;
-#pragma unroll
-        for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, amax_s[wt * C::WF + f][tb][lane & 31]);
-        const float scale = mx > 0.f ? mx / 448.f : 1.f;
-        const float inv = mx > 0.f ? 448.f / mx : 1.f;
-        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
-        const size_t hrow = (size_t)p * C::TM + tok_l;
-        char* hr = hwb + hrow * I;
-#pragma unroll
-        for (int fp = 0; fp < C::FB / 2; ++fp) {
-          const int col0 = j0 + (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            float q[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(hv[tb][fp][g4 * 4 + i] * inv, -448.f), 448.f);
-            __hip_atomic_store(reinterpret_cast<uint32_t*>(hr + col0 + g4 * 8),
-                               pack_e4m3x4(q[0], q[1], q[2], q[3]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        if (wf == 0 && lane < 32)
-          __hip_atomic_store(hsw + hrow * IB + n, scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      tile.epi_l1(a, p, n, j0, amax_s);
+      // publish: every wavefront's h stores have completed before the row
+      // counter moves
       vm_wait<0>();
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (rec) rec[5] = (uint32_t)wall_clock64();
     } else {
-#pragma unroll
-      for (int tb = 0; tb < C::TB; ++tb) {
-        const int mm = m * C::TM + wt * C::TT + tb * 32 + (lane & 31);
-        if (mm < Me) {
-          const int r = r_base + mm;
-          const int f = a.row_pair[r];
-          const float w = a.row_weight[r];
-          const int tok = f / K;
-          const int j = f - tok * K;
-          const int s = tok / T;
-          char* dst = meta.comb[s] + ((size_t)(tok - s * T) * K + j) * H * 2;
-#pragma unroll
-          for (int fb = 0; fb < C::FB; ++fb) {
-            const int col0 = n * C::TN + wf * C::FT + fb * 32 + (lane >> 5) * 4;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const f32x16& v = tile.acc[fb][tb];
-              const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
-                                 ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
-              uint64_t* d = reinterpret_cast<uint64_t*>(dst + (size_t)(col0 + g4 * 8) * 2);
-              if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);
-              else *d = o;
-            }
-          }
-        }
-      }
+      tile.epi_l2(a, n, m, Me, r_base, meta.comb);
       if (rec) {
         vm_wait<0>();
         rec[5] = (uint32_t)wall_clock64();
@@ -465,6 +671,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
 // Cfg8<tokens, features, token waves, feature waves, ring stages>
 using Cfg8Main = Cfg8<128, 256, 2, 2, 3>;   // 128 features x 64 tokens per wavefront
 using Cfg8W8 = Cfg8<128, 256, 2, 4, 3>;     // 64 x 64 per wavefront, two wavefronts per SIMD
+using Cfg8Wide = Cfg8<192, 256, 2, 4, 2, true>;   // 64 features x 96 tokens per wavefront, 16x16x128
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -482,7 +689,8 @@ hipError_t occupancy(int* n) {
 extern const TileInfo kFp8Tiles[];
 extern const int kNumFp8Tiles;
 const TileInfo kFp8Tiles[] = {
-    {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},   // first fitting tile is the default
+    {23, MOE_FP8_E4M3, Cfg8Wide::TM, Cfg8Wide::TN, Cfg8Wide::THREADS},   // first fitting tile is the default
+    {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},
     {21, MOE_FP8_E4M3, Cfg8Main::TM, Cfg8Main::TN, Cfg8Main::THREADS},
 };
 const int kNumFp8Tiles = sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0]);
@@ -491,6 +699,7 @@ hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
   switch (id) {
     case 21: return launch<Cfg8Main>(a, s);
     case 22: return launch<Cfg8W8>(a, s);
+    case 23: return launch<Cfg8Wide>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -499,6 +708,7 @@ hipError_t occupancy_ffn_fp8(int id, int* n) {
   switch (id) {
     case 21: return occupancy<Cfg8Main>(n);
     case 22: return occupancy<Cfg8W8>(n);
+    case 23: return occupancy<Cfg8Wide>(n);
   }
   return hipErrorInvalidValue;
 }
