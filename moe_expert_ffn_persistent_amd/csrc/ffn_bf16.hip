@@ -150,8 +150,7 @@ struct Tile {
   // copy and the MFMAs of a stage run back to back; spread between the MFMAs
   // they overlap.
   template <bool COH>
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, bool issue, size_t off,
-                                          uint32_t slot) {
+  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, size_t off, uint32_t slot) {
     constexpr int KS = C::BK / 16;
     constexpr int NMF = C::FB * C::TB;   // MFMAs per k-step
     constexpr int NL = C::FB + C::TB;    // fragment reads per k-step
@@ -171,11 +170,9 @@ struct Tile {
           for (int q = 0; q < NL; ++q)
             if ((q < NMF ? q : NMF - 1) == m) load_frag(stage, ks + 1, q, wf, wt, af[cur ^ 1], bf[cur ^ 1]);
         }
-        if (issue) {
 #pragma unroll
-          for (int i = 0; i < C::NI; ++i)
-            if (C::issue_slot(i) == ks * NMF + m) issue_one<COH>(i, off, slot);
-        }
+        for (int i = 0; i < C::NI; ++i)
+          if (C::issue_slot(i) == ks * NMF + m) issue_one<COH>(i, off, slot);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -184,7 +181,11 @@ struct Tile {
   // Full K loop over nk stages of BK through an NS-stage LDS ring. Stage kt
   // is awaited (own copies, then one workgroup barrier, after which every
   // wavefront is also done with stage kt-1), then multiplied while the copy of
-  // stage kt+NS-1 goes into the slot stage kt-1 used. acc starts at zero.
+  // stage kt+NS-1 goes into the slot stage kt-1 used. The copy is issued
+  // unconditionally (the last NS-1 stages re-copy stage nk-1 into their free
+  // slot), so no branch splits the MFMA sequence it is spread over; those
+  // extra copies are awaited at the end, before the epilogue reuses LDS.
+  // acc starts at zero.
   template <bool COH>
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
 #pragma unroll
@@ -193,21 +194,22 @@ struct Tile {
       for (int tb = 0; tb < C::TB; ++tb) acc[fb][tb] = f32x16{};
     lds_barrier();   // every wavefront is done with the LDS of the previous tile
 #pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s)
-      if (s < nk) {
+    for (int s = 0; s < C::NS - 1; ++s) {
+      const size_t off = (size_t)min(s, nk - 1) * C::ROW_BYTES;
 #pragma unroll
-        for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, (size_t)s * C::ROW_BYTES, ring + s * C::STAGE_BYTES);
-      }
+      for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, off, ring + s * C::STAGE_BYTES);
+    }
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      vm_wait_ahead<C::NI, C::NS - 2>(min(C::NS - 2, nk - 1 - kt));
+      vm_wait<C::NI * (C::NS - 2)>();   // stage kt has landed (later stages may not have)
       lds_barrier();
-      const int nxt = kt + C::NS - 1;
+      const int nxt = min(kt + C::NS - 1, nk - 1);
       const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, nxt < nk, (size_t)nxt * C::ROW_BYTES,
+      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, (size_t)nxt * C::ROW_BYTES,
                    ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
+    vm_wait<0>();
   }
 };
 
