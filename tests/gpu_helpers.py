@@ -55,6 +55,18 @@ class Uploaded:
             return u.view(np.float32).astype(np.float64).reshape(
                 self.wl.num_tokens, self.wl.top_k, self.wl.hidden)
 
+    def combine_rows_bits(self, flat_pairs) -> np.ndarray:
+        """[len(flat_pairs), H] uint16 of the selected (token, slot) rows,
+        gathered on the device (the full buffer can be several GB)."""
+        idx = torch.as_tensor(np.asarray(flat_pairs, dtype=np.int64), device=dev())
+        rows = self.comb_all.reshape(-1, self.wl.hidden).index_select(0, idx)
+        return rows.cpu().numpy().view(np.uint16)
+
+    def combine_rows_f64(self, flat_pairs) -> np.ndarray:
+        u = self.combine_rows_bits(flat_pairs).astype(np.uint32) << np.uint32(16)
+        with np.errstate(invalid="ignore"):
+            return u.view(np.float32).astype(np.float64)
+
     def combine_bits(self) -> np.ndarray:
         return self.comb_all.cpu().numpy().view(np.uint16).reshape(
             self.wl.num_tokens, self.wl.top_k, self.wl.hidden)

@@ -3,6 +3,8 @@
 Bar: every local combine slot within max|err| <= 1e-2 * max|ref| per row
 (bf16), non-local slots untouched, the two schedules bitwise identical, the
 task trace identical to the CPU model of the schedules."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -313,17 +315,23 @@ def test_fp8_block_scaled_both_schedules(H, I, T, L, k, E, tile):
     assert (outs["expert_wave"] == outs["interleaved"]).all()
 
 
-@pytest.fixture(scope="module")
-def dsv3_full():
-    wl = mi.get_workload("dsv3")
-    return wl, mi.make_inputs(wl)
+FULL_SIZE = ["dsv3", "dsv3_fp8", "dsv3_skew", "qwen3_decode", "qwen3_prefill"]
+
+
+@pytest.fixture(scope="module", params=FULL_SIZE)
+def full_inputs(request):
+    wl = mi.get_workload(request.param)
+    return wl, mi.make_inputs(wl, workers=min(16, os.cpu_count() or 1))
 
 
 @pytest.mark.parametrize("schedule", ["interleaved", "expert_wave"])
-def test_full_size_headline_sampled_rows(dsv3_full, schedule):
-    # the workload and launch configuration bench.py times (automatic plan),
-    # checked on sampled combine rows that the oracle evaluates one by one
-    wl, inp = dsv3_full
+def test_full_size_sampled_rows(full_inputs, schedule):
+    # every workload at full size in the launch configuration bench.py uses
+    # (automatic plan), checked on sampled combine rows that the oracle
+    # evaluates one by one: the first, the last and two random rows of every
+    # local expert; a sample of non-local slots keeps the sentinel and no
+    # routed slot does
+    wl, inp = full_inputs
     up = Uploaded(inp)
     ffn = make_ffn(wl)
     print(f"[ffn] full-size {wl.name} {schedule} tile={ffn.plan.tile} grid={ffn.plan.grid}", flush=True)
@@ -338,18 +346,21 @@ def test_full_size_headline_sampled_rows(dsv3_full, schedule):
     lay = mo.dispatch_layout(idx_ref, wl.local_begin, wl.num_local, ffn.plan.block_m)
     rng = np.random.default_rng(11)
     pairs = []
-    for e in range(wl.num_local):   # first, last and two random rows of every expert
+    for e in range(wl.num_local):
         r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
         if r1 > r0:
-            pairs += [int(lay.row_pair[r]) for r in {r0, r1 - 1, *rng.integers(r0, r1, 2)}]
+            pairs += [int(lay.row_pair[r]) for r in sorted({r0, r1 - 1, *rng.integers(r0, r1, 2)})]
     want = mo.row_outputs(inp, idx_ref, w_ref, pairs)
-    C = up.combine_f64().reshape(-1, wl.hidden)
-    err = row_rel_err(C[pairs], want)
-    assert err.max() <= TOL_BF16, f"max per-row rel err {err.max():.3e}"
-    bits = up.combine_bits().reshape(-1, wl.hidden)
+    err = row_rel_err(up.combine_rows_f64(pairs), want)
+    tol = TOL_FP8 if wl.dtype == "fp8" else TOL_BF16
+    assert err.max() <= tol, f"max per-row rel err {err.max():.3e}"
     nonlocal_ = np.nonzero(lay.pair_row < 0)[0]
-    assert (bits[rng.choice(nonlocal_, 256, replace=False)] == 0xFFFF).all()
-    assert not (bits[lay.row_pair] == 0xFFFF).any()
+    if len(nonlocal_):
+        sample = rng.choice(nonlocal_, min(256, len(nonlocal_)), replace=False)
+        assert (up.combine_rows_bits(sample) == 0xFFFF).all()
+    routed = up.combine_rows_bits(lay.row_pair[rng.choice(len(lay.row_pair), min(2048, len(lay.row_pair)),
+                                                          replace=False)])
+    assert not (routed == 0xFFFF).any()
 
 
 def test_wrapper_rejects_mismatched_buffers_before_launch():
