@@ -446,6 +446,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill-sized experts
 using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
 using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
+using CfgTiny = Cfg<32, 64, 1, 1, 64, 4>;      // one wavefront, 64x32: twice the decode tasks
 using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
 using CfgLarge64 = Cfg<256, 256, 2, 2, 64, 2>;   // 128x128, 128-byte rows, two stages
 using CfgLarge64w8 = Cfg<256, 256, 2, 4, 64, 2>; // 64x128 per wavefront, eight wavefronts
@@ -471,6 +472,7 @@ const TileInfo kBf16Tiles[] = {
     {1, MOE_BF16, CfgLarge::TM, CfgLarge::TN, CfgLarge::THREADS},
     {2, MOE_BF16, CfgMid::TM, CfgMid::TN, CfgMid::THREADS},
     {3, MOE_BF16, CfgSmall::TM, CfgSmall::TN, CfgSmall::THREADS},
+    {4, MOE_BF16, CfgTiny::TM, CfgTiny::TN, CfgTiny::THREADS},
     {5, MOE_BF16, CfgMid64::TM, CfgMid64::TN, CfgMid64::THREADS},
     {6, MOE_BF16, CfgLarge64::TM, CfgLarge64::TN, CfgLarge64::THREADS},
     {7, MOE_BF16, CfgLarge64w8::TM, CfgLarge64w8::TN, CfgLarge64w8::THREADS},
@@ -484,6 +486,7 @@ hipError_t launch_ffn_bf16(int id, const FfnArgs& a, hipStream_t s) {
     case 1: return launch<CfgLarge>(a, s);
     case 2: return launch<CfgMid>(a, s);
     case 3: return launch<CfgSmall>(a, s);
+    case 4: return launch<CfgTiny>(a, s);
     case 5: return launch<CfgMid64>(a, s);
     case 6: return launch<CfgLarge64>(a, s);
     case 7: return launch<CfgLarge64w8>(a, s);
@@ -498,6 +501,7 @@ hipError_t occupancy_ffn_bf16(int id, int* n) {
     case 1: return occupancy<CfgLarge>(n);
     case 2: return occupancy<CfgMid>(n);
     case 3: return occupancy<CfgSmall>(n);
+    case 4: return occupancy<CfgTiny>(n);
     case 5: return occupancy<CfgMid64>(n);
     case 6: return occupancy<CfgLarge64>(n);
     case 7: return occupancy<CfgLarge64w8>(n);
