@@ -45,6 +45,7 @@ extern "C" {
 #define MOE_FFN_ABI_VERSION 1
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
+#define MOE_TRACE_WORDS 10      /* uint32 words per task record */
 
 typedef enum {
   MOE_OK = 0,
@@ -107,17 +108,23 @@ typedef struct {
   int32_t timeout_ms;        /* dependency-wait limit; 0 = 2000 ms                         */
   int32_t* status;           /* device int32, or NULL: set to MOE_ERR_TIMEOUT by a wait
                                 that gave up (never cleared by the library)                */
-  uint32_t* trace;           /* device [grid][trace_capacity][8] task records of each
-                                persistent workgroup, in execution order, or NULL:
+  uint32_t* trace;           /* device [grid][trace_capacity][MOE_TRACE_WORDS] task records
+                                of each persistent workgroup (indexed by its logical
+                                instance), in execution order, or NULL:
                                 word 0 = kind (1 = Linear-1, 2 = Linear-2) | n << 2,
                                 word 1 = scheduler row p,
                                 words 2..5 = low 32 bits of the device wall clock
                                 (moe_plan.wall_clock_khz) at task start, after the
-                                dependency wait, after the mainloop, after the
-                                epilogue's stores were issued (Linear-2) or the row
-                                counter was published (Linear-1); words 6..7 = low
-                                32 bits of the shader clock counter at task start
-                                and after the mainloop.
+                                dependency wait, after the mainloop, and when every
+                                wavefront has issued its epilogue stores (Linear-2:
+                                the sender-visible end of the combine stores;
+                                Linear-1: the row counter was published),
+                                words 6..7 = low 32 bits of the shader clock counter
+                                at task start and after the mainloop,
+                                word 8 = wall clock when the epilogue stores have
+                                completed (Linear-2; equal to word 5 for Linear-1),
+                                word 9 = hardware workgroup id (blockIdx.x; it runs
+                                on XCD word9 mod 8).
                                 Unused records stay untouched                          */
   int32_t trace_capacity;    /* records per workgroup                                      */
   int32_t debug_skip_l1_row; /* testing only: when >= 0, Linear-1 tiles of this scheduler
@@ -213,6 +220,40 @@ int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
 int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,
                           void* const* combine_slices, float* y_local,
                           int32_t* report, void* stream);
+
+/* Parameters of the store burst-gap probe. */
+typedef struct {
+  int32_t producers;        /* K: concurrent producer workgroups, 1..65535            */
+  int32_t bytes_per_burst;  /* B: bytes each producer stores per burst, a positive
+                               multiple of 4096 and of row_bytes                        */
+  int32_t bursts;           /* bursts per producer, >= 1                                */
+  int32_t row_bytes;        /* contiguous bytes per destination row, a power of two
+                               from 16 to 4096; 0 = 512 (one 256-feature bf16 N-tile
+                               piece of a row)                                         */
+  int32_t control;          /* 0: rows scattered over the whole destination buffer with
+                               the combine epilogue's non-temporal stores; 1: rows
+                               confined to its first 256 KiB (L2-resident control)     */
+  int64_t gap_ns;           /* G: idle time of each producer after each burst          */
+} moe_burst_params;
+
+/* Store burst-gap probe: the X-Stage paper's remote-store microbenchmark
+ * (section 3.1, "Remote-Store Microbenchmarks"; notation of Table 1) applied
+ * to the stores this GPU's Linear-2 epilogue makes, scattered rows of local
+ * HBM. K workgroups each issue bytes_per_burst bytes of 16-byte stores into
+ * destination rows at fixed scattered positions, then idle gap_ns, bursts
+ * times. For producer k and burst b, stamps[(k*bursts + b)*2 + 0/1] receive
+ * the low 32 bits of the device wall clock (moe_plan.wall_clock_khz ticks)
+ * just before the first store and once every wavefront of the producer has
+ * issued its last store: their difference is the sender-visible issue time
+ * T_iss, the start-to-start difference of consecutive bursts the period
+ * T_period. From zero-gap, gap-swept and isolated runs the host fits the
+ * model of section 3.2 (Eq. 1-5) and the capacity of section 3.5 (Eq. 6-7).
+ *   dst     device buffer of dst_bytes (>= row_bytes and < 2^32 rows of
+ *           row_bytes; >= 256 KiB with control); its contents are overwritten.
+ *   stamps  device uint32 [producers * bursts * 2].
+ * Enqueued on `stream`; returns MOE_ERR_INVALID_ARG for inconsistent sizes. */
+int32_t moe_store_burst_probe(const moe_burst_params* params, void* dst, size_t dst_bytes,
+                              uint32_t* stamps, void* stream);
 
 #ifdef __cplusplus
 }

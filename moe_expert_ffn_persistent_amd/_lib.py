@@ -24,7 +24,8 @@ MOE_MAX_SLICES = 64
 
 # every symbol include/moe_ffn.h declares
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_scratch_bytes", "moe_ffn_plan",
-           "moe_workspace_init", "moe_dispatch_layout", "moe_ffn_forward", "moe_combine_check")
+           "moe_workspace_init", "moe_dispatch_layout", "moe_ffn_forward", "moe_combine_check",
+           "moe_store_burst_probe")
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -54,7 +55,12 @@ class MoePlan(ctypes.Structure):
                 ("max_sched_rows", c_i32), ("workspace_bytes", ctypes.c_size_t),
                 ("wall_clock_khz", c_i32)]
 
-TRACE_WORDS = 8
+TRACE_WORDS = 10
+
+
+class MoeBurstParams(ctypes.Structure):
+    _fields_ = [("producers", c_i32), ("bytes_per_burst", c_i32), ("bursts", c_i32),
+                ("row_bytes", c_i32), ("control", c_i32), ("gap_ns", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -96,6 +102,8 @@ def load(path: str | None = None):
                                     P(MoeSchedParams), c_vp]
     lib.moe_combine_check.restype = c_i32
     lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp]
+    lib.moe_store_burst_probe.restype = c_i32
+    lib.moe_store_burst_probe.argtypes = [P(MoeBurstParams), c_vp, ctypes.c_size_t, c_vp, c_vp]
     _lib = lib
     return lib
 
@@ -152,3 +160,9 @@ def combine_check(shape, layout, comb_ptrs, y_ptr, report_ptr, stream):
     check(load().moe_combine_check(ctypes.byref(shape), ctypes.byref(layout),
                                    ptr_array(comb_ptrs), y_ptr, report_ptr, stream),
           "moe_combine_check")
+
+
+def store_burst_probe(params: MoeBurstParams, dst_ptr: int, dst_bytes: int, stamps_ptr: int,
+                      stream: int):
+    check(load().moe_store_burst_probe(ctypes.byref(params), dst_ptr, dst_bytes, stamps_ptr, stream),
+          "moe_store_burst_probe")

@@ -342,4 +342,32 @@ int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const
   return launch_check(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int32_t moe_store_burst_probe(const moe_burst_params* prm, void* dst, size_t dst_bytes, uint32_t* stamps,
+                              void* stream) {
+  if (!prm || !dst || !stamps) return MOE_ERR_INVALID_ARG;
+  const int row_bytes = prm->row_bytes > 0 ? prm->row_bytes : 512;
+  if (prm->producers < 1 || prm->producers > 65535 || prm->bursts < 1 || prm->gap_ns < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (row_bytes < 16 || row_bytes > 4096 || (row_bytes & (row_bytes - 1)) || prm->bytes_per_burst <= 0 ||
+      prm->bytes_per_burst % 4096)
+    return MOE_ERR_INVALID_ARG;
+  if (dst_bytes < (size_t)row_bytes || dst_bytes / row_bytes > 0xFFFFFFFFull ||
+      (prm->control && dst_bytes < 256 * 1024))
+    return MOE_ERR_INVALID_ARG;
+  DeviceProps* dp = nullptr;
+  const int32_t st = device_props(&dp);
+  if (st != MOE_OK) return st;
+  BurstArgs a{};
+  a.dst = static_cast<char*>(dst);
+  a.dst_bytes = dst_bytes;
+  a.stamps = stamps;
+  a.producers = prm->producers;
+  a.bytes_per_burst = prm->bytes_per_burst;
+  a.bursts = prm->bursts;
+  a.row_bytes = row_bytes;
+  a.control = prm->control ? 1 : 0;
+  a.gap_ticks = prm->gap_ns * (long long)dp->wall_khz / 1000000;
+  return launch_burst(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // extern "C"

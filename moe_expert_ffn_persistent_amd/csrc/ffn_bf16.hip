@@ -261,7 +261,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     if (t.kind == 0) break;
     const int p = uni(t.p), n = uni(t.n);
     // task record (thread 0 only): kind | n << 2, p, then wall-clock stamps
-    uint32_t* rec = (a.trace && tid == 0 && seq < a.trace_cap)
+    const bool tracing = a.trace && seq < a.trace_cap;   // uniform
+    uint32_t* rec = (tracing && tid == 0)
                         ? a.trace + ((size_t)g * a.trace_cap + seq) * kTraceWords
                         : nullptr;
     if (rec) {
@@ -269,6 +270,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       rec[1] = (uint32_t)p;
       rec[2] = (uint32_t)wall_clock64();
       rec[6] = (uint32_t)__builtin_readcyclecounter();   // shader clock
+      rec[9] = blockIdx.x;
     }
     ++seq;
     const int e = expert_of_row(meta.tile_off, L, p);
@@ -379,7 +381,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       vm_wait<0>();
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (rec) rec[5] = (uint32_t)wall_clock64();
+      if (rec) rec[5] = rec[8] = (uint32_t)wall_clock64();
     } else {
       // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN.
       // Destinations first (one row per thread, independent loads that
@@ -420,10 +422,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
         if (MOE_COMBINE_NT) store16<kStream>(dst + c * 16, v);   // not re-read by this kernel
         else store16<kCacheNormal>(dst + c * 16, v);
       }
-      if (rec) {
-        vm_wait<0>();   // the stamp covers the completion of this wavefront's stores
-        rec[5] = (uint32_t)wall_clock64();
-      }
+      trace_store_span(tracing, rec);
     }
   }
 

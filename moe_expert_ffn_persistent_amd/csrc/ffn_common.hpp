@@ -115,6 +115,18 @@ __device__ __forceinline__ void store16(void* dst, i32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "v"(v) : "memory");
 }
 
+// Trace of an epilogue's stores (`tracing` uniform over the workgroup, `rec`
+// non-null in thread 0 only): word 5 once every wavefront has issued its
+// stores (the sender-visible end), word 8 once they have all completed.
+__device__ __forceinline__ void trace_store_span(bool tracing, uint32_t* rec) {
+  if (!tracing) return;
+  __syncthreads();
+  if (rec) rec[5] = (uint32_t)wall_clock64();
+  vm_wait<0>();
+  __syncthreads();
+  if (rec) rec[8] = (uint32_t)wall_clock64();
+}
+
 // Epilogue staging in LDS: rows of ROWB bytes, 16-byte chunks XOR-swizzled
 // by the row so that a column of lanes (one row each) writes distinct banks
 // and a row of lanes reads whole rows back.

@@ -548,7 +548,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
     const Task t = interleaved ? ist.next() : ews.next();
     if (t.kind == 0) break;
     const int p = uni(t.p), n = uni(t.n);
-    uint32_t* rec = (a.trace && tid == 0 && seq < a.trace_cap)
+    const bool tracing = a.trace && seq < a.trace_cap;   // uniform
+    uint32_t* rec = (tracing && tid == 0)
                         ? a.trace + ((size_t)g * a.trace_cap + seq) * kTraceWords
                         : nullptr;
     if (rec) {
@@ -556,6 +557,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       rec[1] = (uint32_t)p;
       rec[2] = (uint32_t)wall_clock64();
       rec[6] = (uint32_t)__builtin_readcyclecounter();   // shader clock
+      rec[9] = blockIdx.x;
     }
     ++seq;
     const int e = expert_of_row(meta.tile_off, L, p);
@@ -645,13 +647,10 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       vm_wait<0>();
       __syncthreads();
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (rec) rec[5] = (uint32_t)wall_clock64();
+      if (rec) rec[5] = rec[8] = (uint32_t)wall_clock64();
     } else {
       tile.epi_l2(a, n, m, Me, r_base, meta.comb);
-      if (rec) {
-        vm_wait<0>();
-        rec[5] = (uint32_t)wall_clock64();
-      }
+      trace_store_span(tracing, rec);
     }
   }
 

@@ -29,9 +29,24 @@ struct LayoutArgs {
 };
 
 constexpr int kLayoutChunk = 256;    // flat pairs per layout workgroup
-constexpr int kTraceWords = 8;       // uint32 words per task record
+constexpr int kTraceWords = MOE_TRACE_WORDS;   // uint32 words per task record
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+// Store burst-gap probe (burst.hip).
+struct BurstArgs {
+  char* dst;                // destination buffer
+  size_t dst_bytes;
+  uint32_t* stamps;         // [producers][bursts][2] wall clock: issue start, issue end
+  int producers;            // K workgroups
+  int bytes_per_burst;      // B per producer, multiple of 4096 and of row_bytes
+  int bursts;
+  int row_bytes;            // contiguous bytes per destination row, multiple of 16
+  int control;              // 1: rows confined to a 256 KiB region (stays in L2)
+  long long gap_ticks;      // wall-clock ticks of idling after each burst
+};
+
+hipError_t launch_burst(const BurstArgs& a, hipStream_t stream);
 
 // Arguments of the persistent FFN kernel. Passed by value; the slice tables
 // are copied to LDS at kernel start.

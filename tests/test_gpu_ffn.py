@@ -12,6 +12,7 @@ import torch
 import moe_inputs as mi
 from oracle import moe_oracle as mo
 from oracle import schedule as sc
+from moe_expert_ffn_persistent_amd import _lib
 
 pytestmark = pytest.mark.gpu
 
@@ -116,7 +117,7 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
     ref = mo.run(inp, block_m=32)
     up = Uploaded(inp)
     cap = 4096
-    trace = torch.full((grid, cap, 8), -1, dtype=torch.int32, device=dev())
+    trace = torch.full((grid, cap, _lib.TRACE_WORDS), -1, dtype=torch.int32, device=dev())
     ffn = make_ffn(wl, tile=3)
     print(f"[ffn] trace {schedule} grid={grid} D={lead} epw={epw}", flush=True)
     _route_and_layout(ffn, up)
@@ -135,8 +136,10 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
         got = [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used]
         assert got == want[g], f"instance {g}"
         # stamps are ordered within each record: start <= ready <= mainloop end <= done
-        st = used[:, 2:6].astype(np.int64) & 0xFFFFFFFF
+        st = used[:, [2, 3, 4, 5, 8]].astype(np.int64) & 0xFFFFFFFF
         assert (np.diff(st, axis=1) >= 0).all() or (st.max() - st.min() > 2 ** 31)
+        # one hardware workgroup runs the whole stream of instance g
+        assert len(set(used[:, 9].tolist())) == 1
 
 
 @pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
@@ -158,7 +161,7 @@ def test_xcd_placement_by_ntile_changes_nothing_but_placement(schedule):
         plan = ffn.resolved_plan(grid=grid)
         assert plan.n1_tiles == 16
         cap = 2048
-        trace = torch.full((grid, cap, 8), -1, dtype=torch.int32, device=dev())
+        trace = torch.full((grid, cap, _lib.TRACE_WORDS), -1, dtype=torch.int32, device=dev())
         print(f"[ffn] xcd placement {schedule} grid={grid}", flush=True)
         up.reset_combine()
         ffn.forward(up.x_slices, up.w1, up.w2, up.comb_slices, schedule=schedule, grid=grid,
@@ -172,6 +175,15 @@ def test_xcd_placement_by_ntile_changes_nothing_but_placement(schedule):
         for g in range(grid):
             used = tr[g][tr[g][:, 0] != -1]
             assert [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used] == want[g]
+            # placement: block b runs on XCD b % 8; grouped by N-tile (R = N1/8
+            # residues of g mod N1 per XCD) for grid 32, consecutive ids for 24
+            if not len(used):
+                continue
+            b = int(used[0, 9])
+            if grid == 32:
+                assert (g % 16) // 2 == b % 8
+            else:
+                assert g == (b % 8) * (grid // 8) + b // 8
         bits[grid] = up.combine_bits().copy()
     assert (bits[32] == bits[24]).all()
 
