@@ -103,6 +103,28 @@ def _wrap(d):
     return (np.asarray(d, np.int64) + (1 << 32)) % (1 << 32)
 
 
+def burst_concurrency(start, end) -> np.ndarray:
+    """For each interval [start, end) of integer ticks (one per producer and
+    burst; the intervals of one producer do not overlap), the mean number of
+    intervals open over it, itself included: the number of producers issuing
+    alongside it, so that (this count) x B is the aggregate burst volume V of
+    the paper's model. Intervals of zero length count the intervals open at
+    their start."""
+    s = np.asarray(start, np.int64).ravel()
+    e = np.maximum(np.asarray(end, np.int64).ravel(), s)
+    lo = s.min()
+    s, e = s - lo, e - lo
+    n = int(e.max()) + 2
+    diff = np.zeros(n, np.int64)
+    np.add.at(diff, s, 1)
+    np.add.at(diff, e, -1)
+    open_ = np.cumsum(diff)[:-1]                 # intervals open during tick t
+    pre = np.concatenate([[0], np.cumsum(open_)])
+    width = e - s
+    mean = np.where(width > 0, (pre[e] - pre[s]) / np.maximum(width, 1), open_[s] + (width == 0))
+    return mean.reshape(np.shape(start))
+
+
 @dataclass
 class BurstRun:
     K: int
@@ -111,15 +133,29 @@ class BurstRun:
     control: bool
     t_iss: np.ndarray      # [K, bursts] us
     t_period: np.ndarray   # [K, bursts - 1] us
+    kernel_us: float       # launch to completion, every store drained
+    window_us: float       # first burst start to last burst issued, over producers
+    k_eff: np.ndarray      # [K, bursts] producers issuing alongside each burst
 
     @property
     def V(self) -> int:
         return self.K * self.B
 
+    def drained_rate(self) -> float:
+        """Bytes per microsecond over the whole launch: every store of every
+        burst has left the chip's buffers once the kernel has completed."""
+        return self.V * self.t_iss.shape[1] / self.kernel_us
+
     def steady(self, skip: int = 2):
-        """Median issue time and period over producers, after `skip` bursts."""
-        return (float(np.median(self.t_iss[:, skip:])),
-                float(np.median(self.t_period[:, skip:])) if self.t_period.shape[1] > skip else float("nan"))
+        """Mean issue time and period over producers and bursts after the
+        first `skip`: means, not medians, so that bursts x period is the
+        producers' issue time (backpressure stalls are few and long)."""
+        return (float(np.mean(self.t_iss[:, skip:])),
+                float(np.mean(self.t_period[:, skip:])) if self.t_period.shape[1] > skip else float("nan"))
+
+    def v_eff(self, skip: int = 2) -> float:
+        """Aggregate burst volume in flight: mean concurrency x B."""
+        return float(np.mean(self.k_eff[:, skip:])) * self.B
 
 
 def wall_clock_khz() -> int:
@@ -145,74 +181,90 @@ class Prober:
         stamps = torch.zeros(K * bursts * 2, dtype=torch.int32, device=self.device)
         prm = _lib.MoeBurstParams(K, B, bursts, row_bytes, 1 if control else 0, int(gap_us * 1000))
         stream = torch.cuda.current_stream(self.device)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
         _lib.store_burst_probe(prm, self.dst.data_ptr(), self.dst.numel(), stamps.data_ptr(),
                                stream.cuda_stream)
+        ev1.record(stream)
         torch.cuda.synchronize(self.device)
         st = stamps.cpu().numpy().astype(np.int64).reshape(K, bursts, 2) & 0xFFFFFFFF
         us = 1e3 / self.khz
+        rel = _wrap(st - st[:, :, 0].min())
         return BurstRun(K, B, gap_us, control, _wrap(st[:, :, 1] - st[:, :, 0]) * us,
-                        _wrap(st[:, 1:, 0] - st[:, :-1, 0]) * us)
+                        _wrap(st[:, 1:, 0] - st[:, :-1, 0]) * us, ev0.elapsed_time(ev1) * 1e3,
+                        float(rel[:, :, 1].max() * us), burst_concurrency(rel[:, :, 0], rel[:, :, 1]))
 
 
 def calibrate(pr: Prober, K: int = 256) -> dict:
-    """Drain rate from zero-gap periodic bursts, isolated-burst floor and
-    capacity knee, and a gap sweep compared with the model (sections 3.3-3.5).
+    """Drain rate, backpressure-free issue time, capacity and a gap sweep
+    compared with the model (sections 3.3-3.5).
 
-    Every scattered run is paired with the L2-resident control of the same
-    K and B, whose timing has no HBM drain behind it: a scattered period
-    above its control's is backpressure, and only those points enter the fit
-    of R (the drain-dominated regime of section 3.3)."""
+    R is the drained rate of long zero-gap runs: bytes over launch-to-
+    completion time, which includes every store reaching memory. T_iss0 of a
+    burst is the issue time of the L2-resident control of the same K and B
+    (no HBM drain behind it). The aggregate volume V of each burst is its
+    measured concurrency (producers issuing alongside it) times B: the
+    workgroups of one launch do not all issue at once."""
     out = {"K": K}
-    pts = []
+    pts, runs = [], {}
     for k in (K, 2 * K, 4 * K):
         for b_kib in (16, 32, 64, 128, 256):
-            r = pr.run(k, b_kib * KIB, 0.0, bursts=12)
-            c = pr.run(k, b_kib * KIB, 0.0, bursts=12, control=True)
+            r = pr.run(k, b_kib * KIB, 0.0, bursts=24)
+            c = pr.run(k, b_kib * KIB, 0.0, bursts=24, control=True)
+            runs[(k, b_kib * KIB)] = (r, c)
             ti, tp = r.steady()
-            ci, cp = c.steady()
-            pts.append({"K": k, "B": b_kib * KIB, "V": r.V, "t_iss_us": ti, "t_period_us": tp,
-                        "control_t_period_us": cp, "rate_TBps": r.V / tp / 1e6})
-    out["zero_gap"] = pts
-    drain = [p for p in pts if p["V"] >= 8 * 1024 * KIB and p["t_period_us"] > 1.1 * p["control_t_period_us"]]
-    out["drain_points"] = len(drain)
-    if drain:
-        R = fit_drain_rate([p["V"] for p in drain], [p["t_period_us"] for p in drain])
-    else:   # issue-bound everywhere: the highest rate reached bounds R from below
-        R = max(p["V"] / p["t_period_us"] for p in pts)
+            pts.append({"K": k, "B": b_kib * KIB, "t_iss_us": ti, "t_period_us": tp,
+                        "k_eff": r.v_eff() / r.B, "V_eff": r.v_eff(), "t_iss0_us": c.steady()[0],
+                        "kernel_us": r.kernel_us, "drained_TBps": r.drained_rate() / 1e6,
+                        "control_drained_TBps": c.drained_rate() / 1e6})
+    long_runs = [p for p in pts if p["drained_TBps"] * p["kernel_us"] * 1e6 >= 2 ** 30]
+    R = float(np.median([p["drained_TBps"] for p in long_runs])) * 1e6
     out["R_bytes_per_us"] = R
     out["R_TBps"] = R / 1e6
-    # the sweep runs at the point with the most backpressure
-    best = max(pts, key=lambda p: p["t_period_us"] / p["control_t_period_us"])
-    Ks, Bs = best["K"], best["B"]
+    for p in pts:   # Eq. 1 with the measured aggregate volume
+        p["model_t_period_us"] = float(t_period(0.0, p["V_eff"], p["t_iss0_us"], R))
+    out["zero_gap"] = pts
     # isolated bursts (gap well past the drain time) against the control
     iso = []
     for b_kib in (4, 8, 16, 32, 64, 128, 256, 512):
-        V = Ks * b_kib * KIB
-        gap = max(200.0, 3.0 * V / R)
-        r = pr.run(Ks, b_kib * KIB, gap, bursts=3)
-        c = pr.run(Ks, b_kib * KIB, gap, bursts=3, control=True)
-        iso.append({"B": b_kib * KIB, "V": V, "gap_us": gap, "t_iss_us": float(np.median(r.t_iss[:, 1:])),
-                    "t_iss0_us": float(np.median(c.t_iss[:, 1:]))})
-    out["isolated"] = {"K": Ks, "points": iso}
-    out["Q_bytes"] = fit_capacity([p["V"] for p in iso], [p["t_iss_us"] for p in iso],
-                                  [p["t_iss0_us"] for p in iso], R)
-    # gap sweep at that point, scattered and control, gaps in units of V/R
-    V = Ks * Bs
+        gap = max(200.0, 3.0 * K * b_kib * KIB / R)
+        r = pr.run(K, b_kib * KIB, gap, bursts=4)
+        c = pr.run(K, b_kib * KIB, gap, bursts=4, control=True)
+        iso.append({"B": b_kib * KIB, "gap_us": gap, "k_eff": r.v_eff(1) / r.B, "V_eff": r.v_eff(1),
+                    "t_iss_us": float(np.mean(r.t_iss[:, 1:])), "t_iss0_us": float(np.mean(c.t_iss[:, 1:]))})
+    Q = fit_capacity([p["V_eff"] for p in iso], [p["t_iss_us"] for p in iso],
+                     [p["t_iss0_us"] for p in iso], R)
+    for p in iso:
+        p["q_peak0_bytes"] = float(q_peak0(p["V_eff"], p["t_iss0_us"], R))
+        if Q is not None:
+            p["model_t_iss_us"] = float(t_iss_isolated(p["V_eff"], p["t_iss0_us"], R, Q))
+    out["isolated"] = {"K": K, "points": iso}
+    out["Q_bytes"] = Q
+    # gap sweep at the zero-gap point with the most backpressure
+    best = max(pts, key=lambda p: p["t_iss_us"] / p["t_iss0_us"])
+    Ks, Bs = best["K"], best["B"]
+    V0 = best["V_eff"]
     sweep = {}
     for control in (False, True):
         rows = []
         for f in (0.0, 0.25, 0.5, 0.75, 1.0, 1.5, 2.0, 4.0):
-            g = f * V / R
-            r = pr.run(Ks, Bs, g, bursts=10, control=control)
+            g = f * V0 / R
+            r = pr.run(Ks, Bs, g, bursts=12, control=control)
             ti, tp = r.steady()
-            rows.append({"gap_us": g, "t_iss_us": ti, "t_period_us": tp})
+            rows.append({"gap_us": g, "t_iss_us": ti, "t_period_us": tp, "V_eff": r.v_eff()})
         sweep["control" if control else "scattered"] = rows
-    t0 = float(np.median([r["t_iss_us"] for r in sweep["control"]]))
-    for row in sweep["scattered"]:
-        row["model_t_iss_us"] = float(t_iss(row["gap_us"], V, t0, R))
-        row["model_t_period_us"] = float(t_period(row["gap_us"], V, t0, R))
-    out["gap_sweep"] = {"K": Ks, "B": Bs, "V": V, "t_iss0_us": t0, "g_star_us": float(g_star(V, t0, R)),
-                        **sweep}
+    # V of the period law is the volume every resident producer adds per
+    # period, V0 from the zero-gap run (with a gap the producers spread their
+    # issue over the period, so fewer issue at the same instant); T_iss0 at
+    # each gap is the control's issue time at that gap
+    for row, ctl in zip(sweep["scattered"], sweep["control"]):
+        row["model_t_iss_us"] = float(t_iss(row["gap_us"], V0, ctl["t_iss_us"], R))
+        row["model_t_period_us"] = float(t_period(row["gap_us"], V0, ctl["t_iss_us"], R))
+    t0 = sweep["control"][-1]["t_iss_us"]
+    knee = next((row["gap_us"] for row, ctl in zip(sweep["scattered"], sweep["control"])
+                 if row["t_iss_us"] <= 1.1 * ctl["t_iss_us"]), None)
+    out["gap_sweep"] = {"K": Ks, "B": Bs, "V0": V0, "t_iss0_us": t0, "g_star_us": float(g_star(V0, t0, R)),
+                        "measured_knee_us": knee, **sweep}
     return out
 
 
@@ -221,8 +273,8 @@ def calibrate(pr: Prober, K: int = 256) -> dict:
 def tile_spans(trace: np.ndarray, khz: int) -> dict:
     """Per-task spans from an FFN task trace [G, cap, MOE_TRACE_WORDS]:
     Linear-2 sender-visible store span T_RS (words 5 - 4), drain lag after
-    the issue (words 8 - 5), mainloop times, and the number of other Linear-2
-    store spans overlapping each one (K_act)."""
+    the issue (words 8 - 5), mainloop times, and the mean number of Linear-2
+    store spans in flight alongside each one, itself included (K_act)."""
     tr = trace.astype(np.int64) & 0xFFFFFFFF
     used = tr[tr[:, :, 0] != 0xFFFFFFFF]
     if not len(used):
@@ -236,8 +288,8 @@ def tile_spans(trace: np.ndarray, khz: int) -> dict:
     t_rs = (issued - main_end)[l2]
     lag = (done - issued)[l2]
     a, b = main_end[l2], issued[l2]
-    # other Linear-2 store spans overlapping each one
-    k_act = np.array([int(((a < b[i]) & (b > a[i])).sum()) - 1 for i in range(len(a))])
+    # Linear-2 store spans in flight alongside each one, itself included
+    k_act = burst_concurrency(np.round(a * khz / 1e3), np.round(b * khz / 1e3))
     pct = lambda x, q: float(np.percentile(x, q)) if len(x) else float("nan")
     return {
         "l2_tiles": int(l2.sum()),
@@ -270,7 +322,7 @@ def ffn_spans(workload: str = "dsv3") -> dict:
     ffn = MoeExpertFFN(S, T, wl.num_experts, k, wl.local_begin, wl.num_local, H, wl.inter,
                        dtype=wl.dtype, device=dev)
     ffn.layout(logits=up(inp.logits), bias=None if inp.bias is None else up(inp.bias))
-    G, cap = ffn.plan.grid, 256
+    G, cap = ffn.plan.grid, 512
     out = {"workload": wl.name, "tile": ffn.plan.tile, "block_m": ffn.plan.block_m,
            "block_n": ffn.plan.block_n2, "n1": ffn.plan.n1_tiles, "n2": ffn.plan.n2_tiles,
            "combine_bytes_per_tile": ffn.plan.block_m * ffn.plan.block_n2 * 2}
@@ -286,30 +338,45 @@ def ffn_spans(workload: str = "dsv3") -> dict:
     return out
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--workload", default="dsv3")
-    ap.add_argument("--producers", type=int, default=256)
-    args = ap.parse_args(argv)
-    pr = Prober()
-    cal = calibrate(pr, K=args.producers)
-    spans = ffn_spans(args.workload)
+def model_checks(cal: dict, spans: dict) -> dict:
+    """Eq. 14 and Eq. 15 for each schedule of one workload. The stores of a
+    Linear-2 tile are issued by the workgroup that computed it, with nothing
+    else to hide them behind (T_cover = 0), so the whole sender-visible span
+    T_RS reaches the critical path."""
     # T_iss0 = 0 makes Eq. 14 hardest to meet: the check is conservative
     R, t0 = cal["R_bytes_per_us"], 0.0
     checks = {}
     for sched in ("expert_wave", "interleaved"):
-        s = spans[sched]
+        s = spans.get(sched)
         if not s:
             continue
-        # the store spans in flight together: this one and the others overlapping it
-        V = (s["k_act"]["median"] + 1) * spans["combine_bytes_per_tile"]
+        V = s["k_act"]["median"] * spans["combine_bytes_per_tile"]
+        t_rs = s["t_rs_us"]["median"]
         checks[sched] = {
             "V_aggregate_bytes": V,
             "drain_limited_span_us": V / R,
             "eq14_interleave_sufficient": bool(interleave_sufficient(
                 spans["n1"], spans["n2"], V, t0, R, s["mainloop_us"]["l1"], s["mainloop_us"]["l2"])),
+            "eq15_stall_us": float(critical_stall(t_rs, 0.0)),
+            "stall_share_of_l2_tile": t_rs / (t_rs + s["mainloop_us"]["l2"]),
         }
-    print(json.dumps({"calibration": cal, "spans": spans, "model_checks": checks}, default=float), flush=True)
+    return checks
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", default="dsv3", help="comma-separated workload names")
+    ap.add_argument("--producers", type=int, default=256)
+    args = ap.parse_args(argv)
+    pr = Prober()
+    cal = calibrate(pr, K=args.producers)
+    del pr
+    out = {"calibration": cal, "workloads": {}}
+    for name in args.workload.split(","):
+        spans = ffn_spans(name)
+        out["workloads"][name] = {"spans": spans, "model_checks": model_checks(cal, spans)}
+        print(f"[xstage] {name} done", file=sys.stderr, flush=True)
+    print(json.dumps(out, default=float), flush=True)
 
 
 if __name__ == "__main__":

@@ -105,5 +105,22 @@ def test_tile_spans_from_a_hand_made_trace():
     assert s["l2_tiles"] == 2
     assert s["t_rs_us"]["median"] == pytest.approx((5.0 + 2.0) / 2)     # 500 and 200 ticks
     assert s["drain_lag_us"]["median"] == pytest.approx((7.0 + 4.0) / 2)
-    assert s["k_act"]["median"] == 1.0                                  # the two spans overlap
+    # span [8700, 9200) shares 200 of its 500 ticks; [8800, 9000) all of its 200
+    assert s["k_act"]["median"] == pytest.approx((1.4 + 2.0) / 2)
     assert s["mainloop_us"]["l1"] == pytest.approx(40.0)
+
+
+def test_burst_concurrency_counts_open_intervals():
+    # three producers: 0 and 1 overlap for half of 0's burst, 2 stands alone
+    start = np.array([[0, 100], [50, 200], [400, 500]])
+    end = np.array([[100, 150], [150, 260], [450, 500]])
+    c = xs.burst_concurrency(start, end)
+    assert c[0, 0] == pytest.approx(1.5)          # 50 ticks alone, 50 with producer 1
+    assert c[1, 0] == pytest.approx(2.0)          # [50,150): producer 0 issues throughout
+    assert c[0, 1] == pytest.approx(2.0)          # [100,150) inside producer 1's burst
+    assert c[1, 1] == pytest.approx(1.0)
+    assert c[2, 0] == pytest.approx(1.0)
+    assert c[2, 1] == pytest.approx(1.0)          # zero-length burst counts itself
+    # K producers issuing the same interval
+    K = 7
+    assert (xs.burst_concurrency(np.zeros((K, 1)), np.full((K, 1), 10)) == K).all()
