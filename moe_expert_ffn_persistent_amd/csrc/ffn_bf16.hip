@@ -95,16 +95,22 @@ struct Tile {
   // Copy sources: instruction i of wavefront w fills LDS rows
   // [j*RPI, (j+1)*RPI) of a stage, j = w + NW*i; lane l takes row
   // j*RPI + l/CPR and the logical chunk that lands at its physical slot.
-  template <class WRow, class TRow>
-  __device__ __forceinline__ void setup(WRow wrow, TRow trow) {
+  // Instructions below NIW take weight rows (wrow), the others token rows:
+  // every token row's key (tkey, possibly a global load) is fetched before
+  // any is used, so the loads overlap, then taddr maps keys to addresses.
+  template <class WRow, class TKey, class TAddr>
+  __device__ __forceinline__ void setup(WRow wrow, TKey tkey, TAddr taddr) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    int key[C::NI];
+#pragma unroll
+    for (int i = C::NIW; i < C::NI; ++i) key[i] = tkey((wave + C::NW * i) * C::RPI + lane / C::CPR - C::TN);
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) {
       const int j = wave + C::NW * i;
       const int r = j * C::RPI + lane / C::CPR;
       const int c = (lane % C::CPR) ^ ((r >> C::SWZ_SHIFT) & C::SWZ_MASK);
-      const char* base = j * C::RPI < C::TN ? wrow(r) : trow(r - C::TN);
+      const char* base = i < C::NIW ? wrow(r) : taddr(key[i]);
       src[i] = base + c * 16;
     }
   }
@@ -213,6 +219,26 @@ struct Tile {
   }
 };
 
+// Routed pair and router weight of each row of a Linear-2 tile, copied to
+// LDS by the wavefronts before the tile's mainloop copies: older than every
+// stage, they have landed by the first stage's wait, and the epilogue reads
+// them from LDS instead of waiting on global loads. Padding rows repeat the
+// last routed row (their combine rows are never stored).
+template <class C>
+__device__ __forceinline__ void fetch_rows(const int* pair, const float* wgt, int m0, int Me, int* pair_s,
+                                           float* wgt_s, int wave, int lane) {
+  constexpr int NQ = (C::TM + 63) / 64;
+  for (int j = uni(wave); j < 2 * NQ; j += C::NW) {   // uniform over the wavefront
+    const int q = j >> 1;
+    const int r = q * 64 + lane;
+    if (r < C::TM) {
+      const int mm = min(m0 + r, Me - 1);
+      if (j & 1) dma4<kCacheNormal>(reinterpret_cast<const char*>(wgt + mm), (uint32_t)(uintptr_t)(wgt_s + q * 64));
+      else dma4<kCacheNormal>(reinterpret_cast<const char*>(pair + mm), (uint32_t)(uintptr_t)(pair_s + q * 64));
+    }
+  }
+}
+
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
@@ -222,6 +248,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   constexpr bool kRowDstInRing = C::TM * C::TN * 2 + C::TM * (int)sizeof(char*) <= C::LDS_BYTES;
   __shared__ char* rowdst_s[kRowDstInRing ? 1 : C::TM];
   char** const rowdst = kRowDstInRing ? reinterpret_cast<char**>(lds + C::TM * C::TN * 2) : rowdst_s;
+  __shared__ int pair_s[C::TM];
+  __shared__ float wgt_s[C::TM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -238,7 +266,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   }
   __syncthreads();
   if (tid == 0 && a.schedule == MOE_SCHED_EXPERT_WAVE)
-    meta.nwaves = build_waves(meta.tile_off, L, a.N1, a.grid, a.experts_per_wave, meta.wave_row);
+    meta.nwaves = build_waves(meta.tile_off, L, a.N1, a.grid, a.experts_per_wave, meta.wave_exp);
   __syncthreads();
   const int P = uni(meta.tile_off[L]);
   // logical instance id: workgroups are dispatched round-robin over the 8
@@ -251,7 +279,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   ExpertWaveStream ews;
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
   if (interleaved) ist.init(g, G, P, a.N1, a.N2, a.lead_d);
-  else ews.init(g, G, a.N1, a.N2, meta.wave_row, uni(meta.nwaves));
+  else ews.init(g, G, a.N1, a.N2, meta.tile_off, meta.wave_exp, uni(meta.nwaves));
 
   Tile<C> tile;
   tile.ring = (uint32_t)(uintptr_t)lds;
@@ -304,6 +332,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       if (!ok) continue;
       // h is read with device-scope (sc1) copies, which never hit a stale
       // line of this XCD's L2, so no L2 invalidate is needed here
+      fetch_rows<C>(a.row_pair + r_base, a.row_weight + r_base, m * C::TM, Me, pair_s, wgt_s, wave, lane);
     }
     if (rec) rec[3] = (uint32_t)wall_clock64();
 
@@ -319,9 +348,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
             const int wrow = ((blk & 1) ? I : 0) + j0 + (blk >> 1) * 32 + (q & 31);
             return w1e + (size_t)wrow * H * 2;
           },
-          [&](int q) {
-            const int mm = min(m * C::TM + q, Me - 1);
-            const int f = a.row_pair[r_base + mm];
+          [&](int q) { return a.row_pair[r_base + min(m * C::TM + q, Me - 1)]; },
+          [&](int f) {
             const int tok = f / K;
             const int s = tok / T;
             return meta.x[s] + (size_t)(tok - s * T) * H * 2;
@@ -330,7 +358,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       // rows of W2[e] and the block's rows of h
       const char* w2e = static_cast<const char*>(a.w2) + (size_t)e * H * I * 2;
       const char* hb = static_cast<const char*>(a.h);
-      tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; },
+      tile.setup([&](int q) { return w2e + (size_t)(n * C::TN + q) * I * 2; }, [](int q) { return q; },
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
     }
     const int nk = (l1 ? H : I) / C::BK;
@@ -345,16 +373,17 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     // wavefront is past its last stage) and write whole rows: 16-byte stores,
     // a row's bytes contiguous, instead of 8-byte pieces scattered over 32 rows.
     lds_barrier();
+    const int tid_e = opaque(tid), lane_e = tid_e & 63;
     if (l1) {
       // SwiGLU: h[p*TM + token][j0 .. j0 + TN/2) in bf16
       constexpr int HROW = C::TN;   // TN/2 columns x 2 bytes
       static_assert(C::TM * HROW <= C::LDS_BYTES, "h staging fits");
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
-        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
+        const int tok_l = wt * C::TT + tb * 32 + (lane_e & 31);
 #pragma unroll
         for (int fp = 0; fp < C::FB / 2; ++fp) {
-          const int col0 = (wf * (C::FB / 2) + fp) * 32 + (lane >> 5) * 4;
+          const int col0 = (wf * (C::FB / 2) + fp) * 32 + (lane_e >> 5) * 4;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             float hv[4];
@@ -370,7 +399,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       __syncthreads();
       char* hb = static_cast<char*>(a.h) + ((size_t)p * C::TM * I + j0) * 2;
       constexpr int NCH = HROW / 16;
-      for (int idx = tid; idx < C::TM * NCH; idx += C::THREADS) {
+      for (int idx = tid_e; idx < C::TM * NCH; idx += C::THREADS) {
         const int row = idx / NCH, c = idx - row * NCH;
         const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<HROW>(row, c * 16));
         // device scope: written through this XCD's L2 for the consuming XCD
@@ -389,8 +418,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       constexpr int CROW = C::TN * 2;
       static_assert(C::TM * CROW <= C::LDS_BYTES, "combine staging fits");
       const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
-      for (int row = tid; row < rows; row += C::THREADS) {
-        const int f = a.row_pair[r_base + m * C::TM + row];
+      for (int row = tid_e; row < rows; row += C::THREADS) {
+        const int f = pair_s[row];
         const int tok = f / K;
         const int j = f - tok * K;
         const int s = tok / T;
@@ -398,12 +427,11 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       }
 #pragma unroll
       for (int tb = 0; tb < C::TB; ++tb) {
-        const int tok_l = wt * C::TT + tb * 32 + (lane & 31);
-        const int mm = m * C::TM + tok_l;
-        const float w = mm < Me ? a.row_weight[r_base + mm] : 0.f;
+        const int tok_l = wt * C::TT + tb * 32 + (lane_e & 31);
+        const float w = wgt_s[tok_l];
 #pragma unroll
         for (int fb = 0; fb < C::FB; ++fb) {
-          const int col0 = wf * C::FT + fb * 32 + (lane >> 5) * 4;
+          const int col0 = wf * C::FT + fb * 32 + (lane_e >> 5) * 4;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const f32x16& v = tile.acc[fb][tb];
@@ -415,7 +443,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
       }
       __syncthreads();
       constexpr int NCH = CROW / 16;
-      for (int idx = tid; idx < rows * NCH; idx += C::THREADS) {
+      for (int idx = tid_e; idx < rows * NCH; idx += C::THREADS) {
         const int row = idx / NCH, c = idx - row * NCH;
         char* dst = rowdst[row];
         const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<CROW>(row, c * 16));

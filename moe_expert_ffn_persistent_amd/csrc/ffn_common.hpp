@@ -16,7 +16,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 struct Meta {
   int tile_off[MOE_MAX_LOCAL_EXPERTS + 1];
-  int wave_row[MOE_MAX_LOCAL_EXPERTS + 2];
+  uint16_t wave_exp[MOE_MAX_LOCAL_EXPERTS + 2];
   const char* x[MOE_MAX_SLICES];
   char* comb[MOE_MAX_SLICES];
   int nwaves;
@@ -134,6 +134,14 @@ template <int ROWB>
 __device__ __forceinline__ uint32_t stage_off(int row, int byte) {
   constexpr int NCH = ROWB / 16;
   return (uint32_t)(row * ROWB + ((((byte >> 4) ^ row) & (NCH - 1)) << 4) + (byte & 15));
+}
+
+// The value itself, opaque to the optimiser: what an epilogue derives from it
+// (LDS staging addresses) is computed where it is used instead of being
+// hoisted out of the task loop and held, or spilled, across the mainloop.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Four-byte direct-to-LDS copy: lane l's word lands at m0 + 4*l (inactive

@@ -529,7 +529,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   }
   __syncthreads();
   if (tid == 0 && a.schedule == MOE_SCHED_EXPERT_WAVE)
-    meta.nwaves = build_waves(meta.tile_off, L, a.N1, a.grid, a.experts_per_wave, meta.wave_row);
+    meta.nwaves = build_waves(meta.tile_off, L, a.N1, a.grid, a.experts_per_wave, meta.wave_exp);
   __syncthreads();
   const int P = uni(meta.tile_off[L]);
   const int G = a.grid;
@@ -539,7 +539,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   ExpertWaveStream ews;
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
   if (interleaved) ist.init(g, G, P, a.N1, a.N2, a.lead_d);
-  else ews.init(g, G, a.N1, a.N2, meta.wave_row, uni(meta.nwaves));
+  else ews.init(g, G, a.N1, a.N2, meta.tile_off, meta.wave_exp, uni(meta.nwaves));
 
   typename TileOf<C>::type tile;
   tile.ring = (uint32_t)(uintptr_t)lds;

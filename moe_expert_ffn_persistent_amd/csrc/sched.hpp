@@ -54,18 +54,21 @@ struct InterleavedStream {
   }
 };
 
-// Wave boundaries live in LDS: s_wave_row[0..nwaves] are scheduler rows.
+// Wave boundaries live in LDS as expert indices: wave w holds the scheduler
+// rows tile_off[wave_exp[w]] .. tile_off[wave_exp[w + 1]].
 struct ExpertWaveStream {
   int g, G, N1, N2, w, phase, c, nwaves;
-  const int* wave_row;   // LDS
-  __device__ void init(int g_, int G_, int N1_, int N2_, const int* wave_row_, int nwaves_) {
-    g = g_; G = G_; N1 = N1_; N2 = N2_; wave_row = wave_row_; nwaves = nwaves_;
+  const int* tile_off;        // LDS
+  const uint16_t* wave_exp;   // LDS
+  __device__ void init(int g_, int G_, int N1_, int N2_, const int* tile_off_, const uint16_t* wave_exp_,
+                       int nwaves_) {
+    g = g_; G = G_; N1 = N1_; N2 = N2_; tile_off = tile_off_; wave_exp = wave_exp_; nwaves = nwaves_;
     w = 0; phase = 0; c = g_;
   }
   __device__ Task next() {
     while (w < nwaves) {
-      const int r0 = uni(wave_row[w]);
-      const int rows = uni(wave_row[w + 1]) - r0;
+      const int r0 = uni(tile_off[wave_exp[w]]);
+      const int rows = uni(tile_off[wave_exp[w + 1]]) - r0;
       if (phase == 0) {
         if (c < rows * N1) {
           const int q = c / N1;
@@ -91,20 +94,21 @@ struct ExpertWaveStream {
 };
 
 // Greedy wave grouping over local experts, written to LDS by one thread.
-// Returns the number of waves; wave_row gets nwaves + 1 boundaries.
+// Returns the number of waves; wave_exp gets nwaves + 1 boundaries (expert
+// indices, at most L <= MOE_MAX_LOCAL_EXPERTS).
 __device__ inline int build_waves(const int* tile_off, int L, int N1, int G, int experts_per_wave,
-                                  int* wave_row) {
+                                  uint16_t* wave_exp) {
   int nw = 0;
   int start = tile_off[0];
   int n_exp = 0;
-  wave_row[0] = start;
+  wave_exp[0] = 0;
   for (int e = 0; e < L; ++e) {
     ++n_exp;
     const int r1 = tile_off[e + 1];
     const bool full = experts_per_wave > 0 ? (n_exp >= experts_per_wave)
                                            : ((long long)(r1 - start) * N1 >= G);
     if (full || e == L - 1) {
-      if (r1 > start) wave_row[++nw] = r1;
+      if (r1 > start) wave_exp[++nw] = (uint16_t)(e + 1);
       start = r1;
       n_exp = 0;
     }

@@ -297,6 +297,11 @@ def tile_spans(trace: np.ndarray, khz: int) -> dict:
         "drain_lag_us": {"median": pct(lag, 50), "p90": pct(lag, 90)},
         "k_act": {"median": pct(k_act, 50), "p90": pct(k_act, 90)},
         "mainloop_us": {"l1": pct((main_end - ready)[kind == 1], 50), "l2": pct((main_end - ready)[l2], 50)},
+        # Linear-1 epilogue: SwiGLU, h stores completed and published
+        "l1_epilogue_us": {"median": pct((issued - main_end)[kind == 1], 50),
+                           "p90": pct((issued - main_end)[kind == 1], 90)},
+        # task start to operands ready (Linear-2: the wait for h)
+        "ready_wait_us": {"l1": pct((ready - start)[kind == 1], 50), "l2": pct((ready - start)[l2], 50)},
         "span_us": float((done.max() if len(done) else 0.0)),
     }
 
@@ -367,7 +372,15 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="dsv3", help="comma-separated workload names")
     ap.add_argument("--producers", type=int, default=256)
+    ap.add_argument("--spans-only", action="store_true", help="skip the probe calibration")
     args = ap.parse_args(argv)
+    if args.spans_only:
+        out = {"workloads": {}}
+        for name in args.workload.split(","):
+            out["workloads"][name] = {"spans": ffn_spans(name)}
+            print(f"[xstage] {name} done", file=sys.stderr, flush=True)
+        print(json.dumps(out, default=float), flush=True)
+        return 0
     pr = Prober()
     cal = calibrate(pr, K=args.producers)
     del pr
