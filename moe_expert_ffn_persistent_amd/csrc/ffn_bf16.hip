@@ -219,26 +219,6 @@ struct Tile {
   }
 };
 
-// Routed pair and router weight of each row of a Linear-2 tile, copied to
-// LDS by the wavefronts before the tile's mainloop copies: older than every
-// stage, they have landed by the first stage's wait, and the epilogue reads
-// them from LDS instead of waiting on global loads. Padding rows repeat the
-// last routed row (their combine rows are never stored).
-template <class C>
-__device__ __forceinline__ void fetch_rows(const int* pair, const float* wgt, int m0, int Me, int* pair_s,
-                                           float* wgt_s, int wave, int lane) {
-  constexpr int NQ = (C::TM + 63) / 64;
-  for (int j = uni(wave); j < 2 * NQ; j += C::NW) {   // uniform over the wavefront
-    const int q = j >> 1;
-    const int r = q * 64 + lane;
-    if (r < C::TM) {
-      const int mm = min(m0 + r, Me - 1);
-      if (j & 1) dma4<kCacheNormal>(reinterpret_cast<const char*>(wgt + mm), (uint32_t)(uintptr_t)(wgt_s + q * 64));
-      else dma4<kCacheNormal>(reinterpret_cast<const char*>(pair + mm), (uint32_t)(uintptr_t)(pair_s + q * 64));
-    }
-  }
-}
-
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];

@@ -263,7 +263,7 @@ struct Tile8 : Tile8Copies<C> {
   // Linear-1: SwiGLU, per-token amax over the N-tile's 128 h columns
   // (within the lane, across the lane pair l, l+32, then across the feature
   // wavefronts through LDS), e4m3 h and its scale
-  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax) {
+  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax, char*) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wf = wave % C::WF, wt = wave / C::WF;
     float hv[C::TB][C::FB / 2][16];
@@ -310,17 +310,16 @@ struct Tile8 : Tile8Copies<C> {
   }
 
   // Linear-2: bf16(w * acc) into the combine slot of each routed row
-  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, int r_base,
-                                         char* const* comb) {
+  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, char* const* comb, char*,
+                                         const int* pair_s, const float* wgt_s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wf = wave % C::WF, wt = wave / C::WF;
 #pragma unroll
     for (int tb = 0; tb < C::TB; ++tb) {
-      const int mm = m * C::TM + wt * C::TT + tb * 32 + (lane & 31);
-      if (mm < Me) {
-        const int r = r_base + mm;
-        const int f = a.row_pair[r];
-        const float w = a.row_weight[r];
+      const int row = wt * C::TT + tb * 32 + (lane & 31);
+      if (m * C::TM + row < Me) {
+        const int f = pair_s[row];
+        const float w = wgt_s[row];
         const int tok = f / a.k;
         const int j = f - tok * a.k;
         const int s = tok / a.T;
@@ -364,48 +363,66 @@ struct Tile8W : Tile8Copies<C> {
     return sw[sel * kMaxKBlocks + kt];
   }
 
+  // Partial products of the last two blocks of the previous stage and their
+  // scales: they are promoted during the first two MFMAs of the next stage,
+  // so that a wavefront reaches the stage barrier right after issuing its
+  // last MFMA instead of first waiting for the matrix core to finish it.
+  static constexpr int NB = FB16 * TB16;           // output blocks = MFMAs per stage
+  static constexpr int NP = NB % 3 == 0 ? 3 : 4;    // rolling partial registers
+  static_assert(NB % NP == 0, "block b of every stage uses partial register b mod NP");
+  f32x4 part[NP];
+  float s_tail[2];
+
   template <bool COH>
   __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
                                           bool l1, int kt_next, uint32_t slot) {
-    constexpr int NB = FB16 * TB16;   // output blocks = MFMAs per stage
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, c0 = 2 * (lane >> 4);
     i32x8 af[FB16], bf[2];
-#pragma unroll
-    for (int i = 0; i < FB16; ++i) af[i] = this->frag32(stage, wf * C::FT + i * 16 + r16, c0);
+    // Only the first MFMA's operands are read before it: every wavefront
+    // reads LDS at once after the stage barrier, and LDS reads complete in
+    // order, so the remaining weight fragments are read one per MFMA, ahead
+    // of the MFMA that needs them, instead of holding up the first one.
     bf[0] = this->frag32(stage, C::TN + wt * C::TT + r16, c0);
+    af[0] = this->frag32(stage, wf * C::FT + r16, c0);
     const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
     float swv[FB16];
 #pragma unroll
     for (int i = 0; i < FB16; ++i) swv[i] = block_scale(sw, kt, wf, i, l1);
-    f32x4 part[3];
     float stj[2];
     stj[0] = sx[wt * C::TT + r16];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < NB + 2; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const int j = b / FB16, i = b % FB16;   // token block, feature block
-      if (b < NB) {
-        // next token block: its fragment once this block's first MFMA is out,
-        // its scale once the promotions of the block before it are done
-        if (i == 0 && j + 1 < TB16)
-          bf[(j + 1) & 1] = this->frag32(stage, C::TN + wt * C::TT + (j + 1) * 16 + r16, c0);
-        if (i == FB16 / 2 && j + 1 < TB16) stj[(j + 1) & 1] = sx[wt * C::TT + (j + 1) * 16 + r16];
-        // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
-        part[b % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j & 1], f32x4{}, 0, 0, 0, 127,
-                                                                       0, 127);
-      }
-      if (b >= 2) {
-        const int q = b - 2, qj = q / FB16, qi = q % FB16;
+      if (b + 1 < FB16) af[b + 1] = this->frag32(stage, wf * C::FT + (b + 1) * 16 + r16, c0);
+      // next token block: its fragment once this block's first MFMA is out,
+      // its scale once the promotions of the block before it are done
+      if (i == 0 && j + 1 < TB16)
+        bf[(j + 1) & 1] = this->frag32(stage, C::TN + wt * C::TT + (j + 1) * 16 + r16, c0);
+      if (i == FB16 / 2 && j + 1 < TB16) stj[(j + 1) & 1] = sx[wt * C::TT + (j + 1) * 16 + r16];
+      // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
+      part[b % NP] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j & 1], f32x4{}, 0, 0, 0, 127,
+                                                                     0, 127);
+      // promote block b-2: of this stage, or the tail of the previous one
+      const int q = b - 2;
+      if (q >= 0) {
+        const int qj = q / FB16, qi = q % FB16;
         const float s = stj[qj & 1] * swv[qi];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[qi][qj][v] += part[q % 3][v] * s;
+        for (int v = 0; v < 4; ++v) acc[qi][qj][v] += part[q % NP][v] * s;
+      } else if (kt > 0) {
+        const int qi = FB16 + q;   // last token block, feature blocks FB16-2, FB16-1
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[qi][TB16 - 1][v] += part[(q + NP) % NP][v] * s_tail[q + 2];
       }
 #pragma unroll
       for (int k = 0; k < C::NI; ++k)
         if (C::issue_slot(k) == b) this->template issue_one<COH>(k, kt_next, slot);
       __builtin_amdgcn_sched_barrier(0);
     }
+    s_tail[0] = stj[(TB16 - 1) & 1] * swv[FB16 - 2];
+    s_tail[1] = stj[(TB16 - 1) & 1] * swv[FB16 - 1];
   }
 
   template <bool COH>
@@ -415,16 +432,29 @@ struct Tile8W : Tile8Copies<C> {
 #pragma unroll
       for (int j = 0; j < TB16; ++j) acc[i][j] = f32x4{};
     this->template kloop<COH>(*this, lds, nk, wf, wt, sw, l1);
+    // the last stage's tail blocks
+    if (nk > 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        acc[FB16 - 2][TB16 - 1][v] += part[(NB - 2) % NP][v] * s_tail[0];
+        acc[FB16 - 1][TB16 - 1][v] += part[(NB - 1) % NP][v] * s_tail[1];
+      }
+    }
   }
 
   // Linear-1: blocks 0-1 of the wavefront are gate rows, 2-3 the matching up
   // rows (32-row interleave of W1's N-tile); per-token amax over the N-tile's
   // 128 h columns: within the lane (8 values), across the four lanes of a
-  // token column (l, l^16, l^32, l^48), then across the feature wavefronts
-  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // token column (l, l^16, l^32, l^48), then across the feature wavefronts.
+  // The e4m3 h tile is staged in the ring (free once every wavefront is past
+  // the amax exchange) and written as whole 16-byte row pieces.
+  __device__ __forceinline__ void epi_l1(const FfnArgs& a, int p, int n, int j0, float* amax, char* lds) {
+    const int tid = opaque(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6;
     const int wf = wave % C::WF, wt = wave / C::WF;
     const int r16 = lane & 15;
+    constexpr int HROW = C::TN / 2;   // the N-tile's h columns, one byte each
+    static_assert(C::TM * HROW <= C::NS * C::STAGE_BYTES, "h staging fits the ring");
     float hv[TB16][2][4];
 #pragma unroll
     for (int j = 0; j < TB16; ++j) {
@@ -442,7 +472,6 @@ struct Tile8W : Tile8Copies<C> {
       if (lane < 16) amax[wave * C::TT + j * 16 + lane] = mx;
     }
     __syncthreads();
-    char* hwb = static_cast<char*>(a.h);
     const int IB = a.I / 128;
 #pragma unroll
     for (int j = 0; j < TB16; ++j) {
@@ -451,46 +480,69 @@ struct Tile8W : Tile8Copies<C> {
       for (int f = 0; f < C::WF; ++f) mx = fmaxf(mx, amax[(wt * C::WF + f) * C::TT + j * 16 + r16]);
       const float scale = mx > 0.f ? mx / 448.f : 1.f;
       const float inv = mx > 0.f ? 448.f / mx : 1.f;
-      const size_t hrow = (size_t)p * C::TM + wt * C::TT + j * 16 + r16;
-      char* hr = hwb + hrow * a.I + j0 + wf * 32 + 4 * (lane >> 4);
+      const int tok_l = wt * C::TT + j * 16 + r16;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        __hip_atomic_store(reinterpret_cast<uint32_t*>(hr + i * 16), quant4(hv[j][i], inv), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<uint32_t*>(lds + stage_off<HROW>(tok_l, wf * 32 + i * 16 + 4 * (lane >> 4))) =
+            quant4(hv[j][i], inv);
       if (wf == 0 && lane < 16)
-        __hip_atomic_store(a.hs + hrow * IB + n, scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.hs + ((size_t)p * C::TM + tok_l) * IB + n, scale, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    char* hb = static_cast<char*>(a.h) + (size_t)p * C::TM * a.I + j0;
+    constexpr int NCH = HROW / 16;
+    for (int idx = tid; idx < C::TM * NCH; idx += C::THREADS) {
+      const int row = idx / NCH, c = idx - row * NCH;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<HROW>(row, c * 16));
+      // device scope: written through this XCD's L2 for the consuming XCD
+      store16<kCoherent>(hb + (size_t)row * a.I + c * 16, v);
     }
   }
 
-  // Linear-2: bf16(w * acc) into the combine slot of each routed row, four
-  // consecutive features (8 bytes) per lane and block
-  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, int r_base,
-                                         char* const* comb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Linear-2: bf16(w * acc) into the combine slot of each routed row. The
+  // tile is staged in the ring and stored as whole 16-byte row pieces, each
+  // row's destination resolved once (from the routed pairs and weights that
+  // fetch_rows copied to LDS before the mainloop).
+  __device__ __forceinline__ void epi_l2(const FfnArgs& a, int n, int m, int Me, char* const* comb, char* lds,
+                                         const int* pair_s, const float* wgt_s) {
+    const int tid = opaque(threadIdx.x);
+    const int lane = tid & 63, wave = tid >> 6;
     const int wf = wave % C::WF, wt = wave / C::WF;
     const int r16 = lane & 15;
+    constexpr int CROW = C::TN * 2;   // bf16 combine row piece of the N-tile
+    static_assert(C::TM * CROW + C::TM * (int)sizeof(char*) <= C::NS * C::STAGE_BYTES,
+                  "combine staging and row destinations fit the ring");
+    char** const rowdst = reinterpret_cast<char**>(lds + C::TM * CROW);
+    const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
+    lds_barrier();   // every wavefront is past its last stage: the ring is free
+    for (int row = tid; row < rows; row += C::THREADS) {
+      const int f = pair_s[row];
+      const int tok = f / a.k;
+      const int slot = f - tok * a.k;
+      const int s = tok / a.T;
+      rowdst[row] = comb[s] + (((size_t)(tok - s * a.T) * a.k + slot) * a.H + (size_t)n * C::TN) * 2;
+    }
 #pragma unroll
     for (int j = 0; j < TB16; ++j) {
-      const int mm = m * C::TM + wt * C::TT + j * 16 + r16;
-      if (mm < Me) {
-        const int r = r_base + mm;
-        const int f = a.row_pair[r];
-        const float w = a.row_weight[r];
-        const int tok = f / a.k;
-        const int slot = f - tok * a.k;
-        const int s = tok / a.T;
-        char* dst = comb[s] + (((size_t)(tok - s * a.T) * a.k + slot) * a.H + n * C::TN + wf * C::FT +
-                               4 * (lane >> 4)) * 2;
+      const int tok_l = wt * C::TT + j * 16 + r16;
+      const float w = wgt_s[tok_l];
 #pragma unroll
-        for (int i = 0; i < FB16; ++i) {
-          const f32x4& v = acc[i][j];
-          const uint64_t o = (uint64_t)pack_bf16x2(w * v[0], w * v[1]) |
-                             ((uint64_t)pack_bf16x2(w * v[2], w * v[3]) << 32);
-          uint64_t* d = reinterpret_cast<uint64_t*>(dst + i * 32);
-          if (MOE_COMBINE_NT) __builtin_nontemporal_store(o, d);
-          else *d = o;
-        }
+      for (int i = 0; i < FB16; ++i) {
+        const f32x4& v = acc[i][j];
+        const uint64_t o = (uint64_t)pack_bf16x2(w * v[0], w * v[1]) |
+                           ((uint64_t)pack_bf16x2(w * v[2], w * v[3]) << 32);
+        *reinterpret_cast<uint64_t*>(lds + stage_off<CROW>(tok_l, (wf * C::FT + i * 16 + 4 * (lane >> 4)) * 2)) = o;
       }
+    }
+    __syncthreads();
+    constexpr int NCH = CROW / 16;
+    for (int idx = tid; idx < rows * NCH; idx += C::THREADS) {
+      const int row = idx / NCH, c = idx - row * NCH;
+      char* dst = rowdst[row];
+      const i32x4 v = *reinterpret_cast<const i32x4*>(lds + stage_off<CROW>(row, c * 16));
+      if (MOE_COMBINE_NT) store16<kStream>(dst + c * 16, v);   // not re-read by this kernel
+      else store16<kCacheNormal>(dst + c * 16, v);
     }
   }
 };
@@ -511,6 +563,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
   __shared__ Meta8 meta8;
   __shared__ float amax_s[C::NW * C::TT];   // per-token h amax of each wavefront
+  __shared__ int pair_s[C::TM];             // routed pair and router weight of each row of a
+  __shared__ float wgt_s[C::TM];            // Linear-2 tile (fetch_rows)
   Meta& meta = meta8.m;
 
   const int tid = threadIdx.x;
@@ -587,6 +641,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       const int ok = uni(meta.flag);
       __syncthreads();
       if (!ok) continue;
+      fetch_rows<C>(a.row_pair + r_base, a.row_weight + r_base, m * C::TM, Me, pair_s, wgt_s, wave, lane);
     }
     if (rec) rec[3] = (uint32_t)wall_clock64();
 
@@ -641,7 +696,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
     }
 
     if (l1) {
-      tile.epi_l1(a, p, n, j0, amax_s);
+      tile.epi_l1(a, p, n, j0, amax_s, lds);
       // publish: every wavefront's h stores have completed before the row
       // counter moves
       vm_wait<0>();
@@ -649,7 +704,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
       if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (rec) rec[5] = rec[8] = (uint32_t)wall_clock64();
     } else {
-      tile.epi_l2(a, n, m, Me, r_base, meta.comb);
+      tile.epi_l2(a, n, m, Me, meta.comb, lds, pair_s, wgt_s);
       trace_store_span(tracing, rec);
     }
   }
@@ -671,6 +726,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
 using Cfg8Main = Cfg8<128, 256, 2, 2, 3>;   // 128 features x 64 tokens per wavefront
 using Cfg8W8 = Cfg8<128, 256, 2, 4, 3>;     // 64 x 64 per wavefront, two wavefronts per SIMD
 using Cfg8Wide = Cfg8<192, 256, 2, 4, 2, true>;   // 64 features x 96 tokens per wavefront, 16x16x128
+using Cfg8Wide3 = Cfg8<128, 256, 2, 4, 3, true>;  // 64 x 64 per wavefront, 16x16x128, three stages
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -690,6 +746,7 @@ extern const int kNumFp8Tiles;
 const TileInfo kFp8Tiles[] = {
     {23, MOE_FP8_E4M3, Cfg8Wide::TM, Cfg8Wide::TN, Cfg8Wide::THREADS},   // first fitting tile is the default
     {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},
+    {24, MOE_FP8_E4M3, Cfg8Wide3::TM, Cfg8Wide3::TN, Cfg8Wide3::THREADS},
     {21, MOE_FP8_E4M3, Cfg8Main::TM, Cfg8Main::TN, Cfg8Main::THREADS},
 };
 const int kNumFp8Tiles = sizeof(kFp8Tiles) / sizeof(kFp8Tiles[0]);
@@ -699,6 +756,7 @@ hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
     case 21: return launch<Cfg8Main>(a, s);
     case 22: return launch<Cfg8W8>(a, s);
     case 23: return launch<Cfg8Wide>(a, s);
+    case 24: return launch<Cfg8Wide3>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -708,6 +766,7 @@ hipError_t occupancy_ffn_fp8(int id, int* n) {
     case 21: return occupancy<Cfg8Main>(n);
     case 22: return occupancy<Cfg8W8>(n);
     case 23: return occupancy<Cfg8Wide>(n);
+    case 24: return occupancy<Cfg8Wide3>(n);
   }
   return hipErrorInvalidValue;
 }

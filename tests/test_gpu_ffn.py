@@ -301,7 +301,7 @@ def test_h_handoff_across_calls_with_poisoned_workspace(tile):
 TOL_FP8 = 5e-2
 
 
-FP8_TILES = [21, 22, 23]
+FP8_TILES = [21, 22, 23, 24]
 
 
 @pytest.mark.parametrize("tile", FP8_TILES)
