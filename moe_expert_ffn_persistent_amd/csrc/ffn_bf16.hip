@@ -44,7 +44,7 @@ namespace moe {
 namespace {
 
 
-template <int TM_, int TN_, int WT_, int WF_, int BK_, int NS_>
+template <int TM_, int TN_, int WT_, int WF_, int BK_, int NS_, int SP_ = MOE_ISSUE_SPREAD>
 struct Cfg {
   static constexpr int TM = TM_;          // tokens per M-block (b_m)
   static constexpr int TN = TN_;          // features per N-tile (b_n)
@@ -71,8 +71,12 @@ struct Cfg {
   static constexpr int NIW = TN / RPI / NW;       // of which weight rows (the first NIW)
   static constexpr int NM = (BK / 16) * (TT / 32) * (FT / 32);   // MFMAs per wavefront per stage
   // copy instruction i of a stage is issued after MFMA issue_slot(i) of the
-  // stage before: spread evenly over the first MOE_ISSUE_SPREAD/8 of the MFMAs
-  static constexpr int issue_slot(int i) { return i * NM * MOE_ISSUE_SPREAD / (NI * 8); }
+  // stage before: spread evenly over the first SP/8 of the MFMAs (measured
+  // per tile on MI355X: the HBM-bound 160 x 256 tile gains from spreading
+  // the copies wider, the MFMA-bound 256 x 256 tiles from issuing earlier)
+  static constexpr int SP = SP_;
+  static_assert(SP >= 1 && SP <= 8, "spread in eighths of the stage");
+  static constexpr int issue_slot(int i) { return i * NM * SP / (NI * 8); }
   static constexpr int A_BYTES = TN * ROW_BYTES;
   static constexpr int STAGE_BYTES = (TN + TM) * ROW_BYTES;
   // LDS: the copy ring, reused by the epilogue to stage a TM x TN bf16 tile
@@ -454,9 +458,9 @@ using CfgLarge = Cfg<256, 256, 2, 2, 32, 4>;   // 128x128 per wavefront: prefill
 using CfgMid = Cfg<192, 256, 2, 2, 32, 5>;     // 128x96: ~100-190 rows per expert, weights read once
 using CfgSmall = Cfg<32, 128, 1, 2, 64, 3>;    // 64x32: decode-sized experts
 using CfgTiny = Cfg<32, 64, 1, 1, 64, 4>;      // one wavefront, 64x32: twice the decode tasks
-using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3>;   // 64x160, 128-byte rows per stage
+using CfgMid64 = Cfg<160, 256, 1, 4, 64, 3, 6>;   // 64x160, 128-byte rows per stage
 using CfgLarge64 = Cfg<256, 256, 2, 2, 64, 2>;   // 128x128, 128-byte rows, two stages
-using CfgLarge64w8 = Cfg<256, 256, 2, 4, 64, 2>; // 64x128 per wavefront, eight wavefronts
+using CfgLarge64w8 = Cfg<256, 256, 2, 4, 64, 2, 2>; // 64x128 per wavefront, eight wavefronts
 using CfgLarge32w8 = Cfg<256, 256, 2, 4, 32, 4>; // as 7 with 64-byte rows and four stages
 using CfgLarge32w8s3 = Cfg<256, 256, 2, 4, 32, 3>;
 

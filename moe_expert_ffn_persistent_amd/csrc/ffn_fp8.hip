@@ -31,7 +31,7 @@
 namespace moe {
 namespace {
 
-template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false>
+template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false, int SP_ = MOE_ISSUE_SPREAD>
 struct Cfg8 {
   static constexpr int TM = TM_, TN = TN_, WT = WT_, WF = WF_, NS = NS_;
   // WIDE: 16x16x128 MFMAs (one per output block and K block), promoted
@@ -56,8 +56,11 @@ struct Cfg8 {
   static constexpr int NM = WIDE ? (FT / 16) * (TT / 16) : 2 * FB * TB;
   // MFMA of the first step after which the second step's fragments are read
   static constexpr int FRAG1_AFTER = NW >= 8 ? FB * TB - 1 : 0;
-  // copy i of a stage is issued after MFMA issue_slot(i) of the stage before
-  static constexpr int issue_slot(int i) { return i * NM * MOE_ISSUE_SPREAD / (NI * 8); }
+  // copy i of a stage is issued after MFMA issue_slot(i) of the stage
+  // before: spread evenly over the first SP/8 of the MFMAs
+  static constexpr int SP = SP_;
+  static_assert(SP >= 1 && SP <= 8, "spread in eighths of the stage");
+  static constexpr int issue_slot(int i) { return i * NM * SP / (NI * 8); }
   static_assert(TN == 256, "an N-tile must own exactly one 128-column h-scale block");
   static_assert(TM % 64 == 0 && TM <= 64 * NW, "token-scale copies cover the M-block");
   static_assert(TT % 32 == 0 && FT % 32 == 0 && FB % 2 == 0, "wavefront tile");
@@ -725,7 +728,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
 // Cfg8<tokens, features, token waves, feature waves, ring stages>
 using Cfg8Main = Cfg8<128, 256, 2, 2, 3>;   // 128 features x 64 tokens per wavefront
 using Cfg8W8 = Cfg8<128, 256, 2, 4, 3>;     // 64 x 64 per wavefront, two wavefronts per SIMD
-using Cfg8Wide = Cfg8<192, 256, 2, 4, 2, true>;   // 64 features x 96 tokens per wavefront, 16x16x128
+using Cfg8Wide = Cfg8<192, 256, 2, 4, 2, true, 2>;   // 64 features x 96 tokens per wavefront, 16x16x128
 using Cfg8Wide3 = Cfg8<128, 256, 2, 4, 3, true>;  // 64 x 64 per wavefront, 16x16x128, three stages
 
 template <class C>
