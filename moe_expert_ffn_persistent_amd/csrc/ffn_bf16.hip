@@ -76,7 +76,7 @@ struct Cfg {
   // the copies wider, the MFMA-bound 256 x 256 tiles from issuing earlier)
   static constexpr int SP = SP_;
   static_assert(SP >= 1 && SP <= 8, "spread in eighths of the stage");
-  static constexpr int issue_slot(int i) { return i * NM * SP / (NI * 8); }
+  static constexpr int issue_slot(int i, int nm = NM) { return i * nm * SP / (NI * 8); }
   static constexpr int A_BYTES = TN * ROW_BYTES;
   static constexpr int STAGE_BYTES = (TN + TM) * ROW_BYTES;
   // LDS: the copy ring, reused by the epilogue to stage a TM x TN bf16 tile
@@ -159,11 +159,14 @@ struct Tile {
   // hold the wavefront at the issue until the address unit drains them, so the
   // copy and the MFMAs of a stage run back to back; spread between the MFMAs
   // they overlap.
-  template <bool COH>
+  // Only the first NTB token blocks are multiplied (the others hold padding
+  // rows only); the copies are spread over the MFMAs that remain.
+  template <bool COH, int NTB>
   __device__ __forceinline__ void compute(const char* stage, int wf, int wt, size_t off, uint32_t slot) {
     constexpr int KS = C::BK / 16;
-    constexpr int NMF = C::FB * C::TB;   // MFMAs per k-step
-    constexpr int NL = C::FB + C::TB;    // fragment reads per k-step
+    constexpr int NMF = C::FB * NTB;     // MFMAs per k-step
+    constexpr int NL = C::FB + NTB;      // fragment reads per k-step
+    static_assert(NTB >= 1 && NTB <= C::TB, "active token blocks");
     bf16x8 af[2][C::FB], bf[2][C::TB];
 #pragma unroll
     for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
@@ -173,7 +176,7 @@ struct Tile {
       const int cur = ks & 1;
 #pragma unroll
       for (int m = 0; m < NMF; ++m) {
-        const int fb = m / C::TB, tb = m % C::TB;
+        const int fb = m / NTB, tb = m % NTB;
         acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][fb], bf[cur][tb], acc[fb][tb], 0, 0, 0);
         if (ks + 1 < KS) {
 #pragma unroll
@@ -182,7 +185,7 @@ struct Tile {
         }
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
-          if (C::issue_slot(i) == ks * NMF + m) issue_one<COH>(i, off, slot);
+          if (C::issue_slot(i, KS * NMF) == ks * NMF + m) issue_one<COH>(i, off, slot);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -195,8 +198,8 @@ struct Tile {
   // unconditionally (the last NS-1 stages re-copy stage nk-1 into their free
   // slot), so no branch splits the MFMA sequence it is spread over; those
   // extra copies are awaited at the end, before the epilogue reuses LDS.
-  // acc starts at zero.
-  template <bool COH>
+  // acc starts at zero; token blocks NTB and up stay zero.
+  template <bool COH, int NTB = C::TB>
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
@@ -215,13 +218,17 @@ struct Tile {
       lds_barrier();
       const int nxt = min(kt + C::NS - 1, nk - 1);
       const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, (size_t)nxt * C::ROW_BYTES,
-                   ring + nslot * C::STAGE_BYTES);
+      compute<COH, NTB>(lds + slot * C::STAGE_BYTES, wf, wt, (size_t)nxt * C::ROW_BYTES,
+                        ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
     vm_wait<0>();
   }
 };
+
+// token blocks multiplied for an M-block whose last token block is padding
+template <class C>
+constexpr int short_tb() { return C::WT == 1 && C::TB > 1 ? C::TB - 1 : C::TB; }
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
@@ -346,8 +353,17 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
                  [&](int q) { return hb + ((size_t)p * C::TM + q) * I * 2; });
     }
     const int nk = (l1 ? H : I) / C::BK;
-    if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt);
-    else tile.template mainloop<true>(lds, nk, wf, wt);
+    // With one wavefront along the tokens, an M-block whose last 32-token
+    // block holds only padding rows skips that block's MFMAs (an expert of
+    // 101-128 rows in a 160-row block).
+    const bool short_blk = C::WT == 1 && C::TB > 1 && Me - m * C::TM <= C::TM - 32;
+    if (short_blk) {
+      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false, short_tb<C>()>(lds, nk, wf, wt);
+      else tile.template mainloop<true, short_tb<C>()>(lds, nk, wf, wt);
+    } else {
+      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt);
+      else tile.template mainloop<true>(lds, nk, wf, wt);
+    }
     if (rec) {
       rec[4] = (uint32_t)wall_clock64();
       rec[7] = (uint32_t)__builtin_readcyclecounter();
