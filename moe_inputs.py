@@ -3,7 +3,9 @@
 This module is shared by the CPU oracle and the HIP path. It holds no step of
 the method's arithmetic: no routing, no layout, no FFN and no combine. It only
 draws seeded random numbers and packs them into the byte formats that both
-sides receive (bf16 bit patterns; e4m3 bytes plus fp32 block scales).
+sides receive (bf16 bit patterns; e4m3 bytes plus fp32 block scales; OCP MX
+blocks of 32 elements: e2m1 weights packed two per byte, e4m3 activations,
+each block with one E8M0 power-of-two scale).
 
 Workload shapes follow the X-Stage paper's MegaMoE evaluation (section 5.1,
 expert parallelism over eight ranks: eight source slices stand in for the
@@ -32,7 +34,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get_workload", "MoeInputs", "make_inputs",
-    "f32_to_bf16_bits", "quantize_e4m3_blocks", "e4m3_encode",
+    "f32_to_bf16_bits", "quantize_e4m3_blocks", "e4m3_encode", "e2m1_encode",
+    "quantize_mx_e4m3", "quantize_mx_e2m1",
 ]
 
 
@@ -47,7 +50,8 @@ class Workload:
     num_local: int           # L: local experts on this GPU
     hidden: int              # H
     inter: int               # I
-    dtype: str               # "bf16" or "fp8" (e4m3 with fp32 block scales)
+    dtype: str               # "bf16", "fp8" (e4m3 with fp32 block scales) or
+                             # "w4a8" (MX: e2m1 weights, e4m3 activations)
     skew: bool               # Zipf-biased router logits
     seed: int
 
@@ -68,6 +72,7 @@ WORKLOADS = {
         Workload("dsv3_fp8", 8, 4096, 256, 8, 0, 32, 7168, 2048, "fp8", False, 1004),
         Workload("qwen3_decode", 8, 16, 128, 8, 0, 16, 4096, 1536, "bf16", False, 1005),
         Workload("qwen3_prefill", 8, 8192, 128, 8, 0, 16, 4096, 1536, "bf16", False, 1006),
+        Workload("dsv3_w4a8", 8, 4096, 256, 8, 0, 32, 7168, 2048, "w4a8", False, 1007),
     ]
 }
 
@@ -126,17 +131,76 @@ def quantize_e4m3_blocks(a: np.ndarray, block_rows: int, block_cols: int):
     return codes, scale
 
 
+# OCP Microscaling (MX) formats: blocks of 32 consecutive elements along a
+# row share one E8M0 scale 2^(byte - 127). The block exponent is
+# floor(log2(amax)) minus the element format's largest exponent (2 for e2m1,
+# whose largest value is 6 = 1.5 * 2^2; 8 for e4m3, 448 = 1.75 * 2^8), and
+# elements are value / 2^exponent rounded to nearest-even in the element
+# format, clamped to its largest magnitude. An all-zero block gets scale 1.
+MX_BLOCK = 32
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """Encode values as OCP FP4 E2M1 codes (sign bit 3, two exponent bits of
+    bias 1, one mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), rounding
+    to nearest with ties to the even code and saturating to +-6. Returns one
+    code (0..15) per element as uint8."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - _E2M1_GRID)              # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d <= best                                   # nearest, both codes on a tie
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    sign = np.signbit(v) & (idx > 0)
+    return (idx | (sign.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def _mx_exponents(a: np.ndarray, emax: int) -> np.ndarray:
+    """Per-block exponent for [R, C] values: [R, C/32] int."""
+    R, C = a.shape
+    assert C % MX_BLOCK == 0
+    amax = np.abs(a.reshape(R, C // MX_BLOCK, MX_BLOCK)).max(axis=2).astype(np.float64)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64) - emax
+    return np.where(amax > 0, e, 0)
+
+
+def quantize_mx_e4m3(a: np.ndarray):
+    """MX e4m3 of a 2-D array: (codes uint8 [R, C], E8M0 scale bytes uint8 [R, C/32])."""
+    a = np.asarray(a, dtype=np.float32)
+    R, C = a.shape
+    e = _mx_exponents(a, 8)
+    q = a.astype(np.float64) / np.ldexp(1.0, np.repeat(e, MX_BLOCK, axis=1))
+    codes = e4m3_encode(np.clip(q, -448.0, 448.0).astype(np.float32))
+    return codes, (e + 127).astype(np.uint8)
+
+
+def quantize_mx_e2m1(a: np.ndarray):
+    """MX e2m1 of a 2-D array: (packed uint8 [R, C/2] with element 2i in the
+    low nibble of byte i and 2i+1 in the high nibble, E8M0 scale bytes uint8
+    [R, C/32])."""
+    a = np.asarray(a, dtype=np.float32)
+    R, C = a.shape
+    e = _mx_exponents(a, 2)
+    q = a.astype(np.float64) / np.ldexp(1.0, np.repeat(e, MX_BLOCK, axis=1))
+    codes = e2m1_encode(q)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))
+    return packed.astype(np.uint8), (e + 127).astype(np.uint8)
+
+
 @dataclasses.dataclass
 class MoeInputs:
     wl: Workload
     logits: np.ndarray            # fp32 [N, E]
     bias: np.ndarray | None       # fp32 [E] or None
     x: np.ndarray                 # bf16 bits uint16 [N, H], or e4m3 codes uint8 [N, H]
-    x_scale: np.ndarray | None    # fp32 [N, H/128] (fp8 only)
-    w1: np.ndarray                # [L, 2I, H] bf16 bits or e4m3 codes
-    w1_scale: np.ndarray | None   # fp32 [L, 2I/128, H/128] (fp8 only)
-    w2: np.ndarray                # [L, H, I]
-    w2_scale: np.ndarray | None   # fp32 [L, H/128, I/128] (fp8 only)
+    x_scale: np.ndarray | None    # fp8: fp32 [N, H/128]; w4a8: E8M0 uint8 [N, H/32]
+    w1: np.ndarray                # [L, 2I, H] bf16 bits or e4m3 codes; w4a8: packed
+                                  # e2m1 uint8 [L, 2I, H/2]
+    w1_scale: np.ndarray | None   # fp8: fp32 [L, 2I/128, H/128]; w4a8: E8M0 [L, 2I, H/32]
+    w2: np.ndarray                # [L, H, I] (w4a8: [L, H, I/2] packed e2m1)
+    w2_scale: np.ndarray | None   # fp8: fp32 [L, H/128, I/128]; w4a8: E8M0 [L, H, I/32]
 
 
 def _children(seed: int):
@@ -171,6 +235,8 @@ def make_x(wl: Workload):
     x = _normal(ch[1], (wl.num_tokens, wl.hidden))
     if wl.dtype == "fp8":
         return quantize_e4m3_blocks(x, 1, 128)
+    if wl.dtype == "w4a8":
+        return quantize_mx_e4m3(x)
     return f32_to_bf16_bits(x), None
 
 
@@ -184,6 +250,10 @@ def make_expert_weights(wl: Workload, e: int):
     if wl.dtype == "fp8":
         q1, s1_ = quantize_e4m3_blocks(w1, 128, 128)
         q2, s2_ = quantize_e4m3_blocks(w2, 128, 128)
+        return q1, s1_, q2, s2_
+    if wl.dtype == "w4a8":
+        q1, s1_ = quantize_mx_e2m1(w1)
+        q2, s2_ = quantize_mx_e2m1(w2)
         return q1, s1_, q2, s2_
     return f32_to_bf16_bits(w1), None, f32_to_bf16_bits(w2), None
 
@@ -220,18 +290,24 @@ def make_inputs(wl: Workload, experts: int | None = None, workers: int = 1) -> M
     logits, bias = make_logits(wl)
     x, xs = make_x(wl)
     L = wl.num_local
-    wdt = np.uint8 if wl.dtype == "fp8" else np.uint16
+    wdt = np.uint16 if wl.dtype == "bf16" else np.uint8
+    pack = 2 if wl.dtype == "w4a8" else 1      # e2m1: two elements per byte
     jobs = [(wl, e) for e in range(L if experts is None else min(experts, L))]
     parallel = workers > 1 and len(jobs) > 1
     alloc = _shared_array if parallel else (lambda shape, dt: np.zeros(shape, dt))
-    w1 = alloc((L, 2 * wl.inter, wl.hidden), wdt)
-    w2 = alloc((L, wl.hidden, wl.inter), wdt)
+    w1 = alloc((L, 2 * wl.inter, wl.hidden // pack), wdt)
+    w2 = alloc((L, wl.hidden, wl.inter // pack), wdt)
     w1s = w2s = None
     if wl.dtype == "fp8":
         w1s = alloc((L, 2 * wl.inter // 128, wl.hidden // 128), np.float32)
         w2s = alloc((L, wl.hidden // 128, wl.inter // 128), np.float32)
         w1s[...] = 1.0
         w2s[...] = 1.0
+    elif wl.dtype == "w4a8":
+        w1s = alloc((L, 2 * wl.inter, wl.hidden // MX_BLOCK), np.uint8)
+        w2s = alloc((L, wl.hidden, wl.inter // MX_BLOCK), np.uint8)
+        w1s[...] = 127
+        w2s[...] = 127
     _SHARED.update(w1=w1, w2=w2, w1s=w1s, w2s=w2s)
     try:
         if parallel:

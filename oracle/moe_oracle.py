@@ -21,8 +21,9 @@ independent tiles only, so they do not change this result.
 Precision: floating point is evaluated in float64. Two decisions that turn
 floating point into integers are taken in float32, the precision of the
 kernel: the biased router logit z = logit + bias, and the top-k selection on
-z. Inputs are the exact bytes the GPU receives (bf16 bit patterns, or e4m3
-codes with their fp32 block scales), decoded exactly.
+z. Inputs are the exact bytes the GPU receives (bf16 bit patterns, e4m3
+codes with their fp32 block scales, or OCP MX blocks: e2m1 weights and e4m3
+activations with one E8M0 scale per 32 elements), decoded exactly.
 
 Readings where the pages are silent (each is listed in the design notes):
   * top-k order: descending z, equal z broken by the lower expert index;
@@ -43,7 +44,8 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "bf16_bits_to_f64", "e4m3_to_f64", "dequant_blocks", "route", "Layout",
+    "bf16_bits_to_f64", "e4m3_to_f64", "e2m1_to_f64", "e8m0_to_f64", "unpack_e2m1",
+    "dequant_blocks", "dequant_mx", "route", "Layout",
     "dispatch_layout", "swiglu", "expert_ffn", "combine", "local_reduce",
     "OracleResult", "run", "scheduler_rows",
 ]
@@ -72,6 +74,40 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     sub = s * np.ldexp(M / 8.0, -6)
     out = np.where(E == 0, sub, normal)
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e2m1_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP 4-bit floating point E2M1 (MX specification): sign bit 3, exponent
+    bits 2..1 with bias 1, mantissa bit 0, no infinities or NaN. Normal
+    (E > 0): (-1)^s * 2^(E-1) * (1 + M/2); subnormal (E = 0): (-1)^s * M/2."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    s = np.where(c & 0x8, -1.0, 1.0)
+    E = (c >> 1) & 0x3
+    M = c & 0x1
+    return np.where(E == 0, s * M / 2.0, s * np.ldexp(1.0 + M / 2.0, E - 1))
+
+
+def e8m0_to_f64(b: np.ndarray) -> np.ndarray:
+    """OCP E8M0 scale: 2^(b - 127); 0xFF is NaN."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
+    """Two e2m1 codes per byte along the last axis, element 2i in the low
+    nibble of byte i: [..., C/2] bytes -> [..., C] codes."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequant_mx(values: np.ndarray, scale_bytes: np.ndarray, block: int = 32) -> np.ndarray:
+    """MX block scaling: element (r, c) times the E8M0 scale of block
+    (r, c // block)."""
+    s = np.repeat(e8m0_to_f64(scale_bytes), block, axis=-1)
+    return np.asarray(values, np.float64) * s
 
 
 def dequant_blocks(codes: np.ndarray, scales: np.ndarray, br: int, bc: int) -> np.ndarray:
@@ -204,16 +240,25 @@ class OracleResult:
     y_local: np.ndarray    # [N, H]
 
 
-def decode_x(inp) -> np.ndarray:
+def decode_x_rows(inp, rows=slice(None)) -> np.ndarray:
     if inp.wl.dtype == "fp8":
-        return dequant_blocks(inp.x, inp.x_scale, 1, 128)
-    return bf16_bits_to_f64(inp.x)
+        return dequant_blocks(inp.x[rows], inp.x_scale[rows], 1, 128)
+    if inp.wl.dtype == "w4a8":
+        return dequant_mx(e4m3_to_f64(inp.x[rows]), inp.x_scale[rows])
+    return bf16_bits_to_f64(inp.x[rows])
+
+
+def decode_x(inp) -> np.ndarray:
+    return decode_x_rows(inp)
 
 
 def decode_expert(inp, e: int):
     if inp.wl.dtype == "fp8":
         return (dequant_blocks(inp.w1[e], inp.w1_scale[e], 128, 128),
                 dequant_blocks(inp.w2[e], inp.w2_scale[e], 128, 128))
+    if inp.wl.dtype == "w4a8":
+        return (dequant_mx(e2m1_to_f64(unpack_e2m1(inp.w1[e])), inp.w1_scale[e]),
+                dequant_mx(e2m1_to_f64(unpack_e2m1(inp.w2[e])), inp.w2_scale[e]))
     return bf16_bits_to_f64(inp.w1[e]), bf16_bits_to_f64(inp.w2[e])
 
 
@@ -247,7 +292,7 @@ def row_outputs(inp, idx, w, pairs, block_m: int = 128):
     the whole oracle would take too long."""
     wl = inp.wl
     k = wl.top_k
-    x = decode_x(inp) if wl.dtype != "fp8" else None
+    x = decode_x(inp) if wl.dtype == "bf16" else None
     out = np.zeros((len(pairs), wl.hidden), dtype=np.float64)
     by_e = {}
     for i, f in enumerate(pairs):
@@ -255,10 +300,7 @@ def row_outputs(inp, idx, w, pairs, block_m: int = 128):
     for e, ids in by_e.items():
         W1, W2 = decode_expert(inp, e)
         toks = [int(pairs[i]) // k for i in ids]
-        if x is None:
-            X = dequant_blocks(inp.x[toks], inp.x_scale[toks], 1, 128)
-        else:
-            X = x[toks]
+        X = decode_x_rows(inp, toks) if x is None else x[toks]
         Yr = expert_ffn(X, W1, W2)
         for r, i in enumerate(ids):
             out[i] = np.asarray(w, np.float64).reshape(-1)[pairs[i]] * Yr[r]

@@ -311,3 +311,87 @@ def test_sampled_rows_match_full_oracle():
     got = mo.row_outputs(inp, r.idx, r.w, pairs)
     want = r.C.reshape(-1, wl.hidden)[pairs]
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-13 * np.abs(want).max())
+
+
+# --------------------------------------------------------------------------
+# OCP MX formats (the W4A8 workload): e2m1 weights, e4m3 activations, E8M0
+# block scales over 32 elements
+# --------------------------------------------------------------------------
+
+def test_e2m1_decode_spec_values():
+    # OCP Microscaling Formats (MX) v1.0, FP4 E2M1: exponent bias 1, one
+    # mantissa bit, no infinities or NaN
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = mo.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    assert list(got[:8]) == want
+    assert list(got[8:]) == [-v for v in want]
+
+
+def test_e8m0_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    got = mo.e8m0_to_f64(codes)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    assert mo.e8m0_to_f64(np.array([127, 128, 120], np.uint8)).tolist() == [1.0, 2.0, 2.0 ** -7]
+
+
+def test_e2m1_packing_low_nibble_first():
+    # bytes 0x21, 0xF7 hold codes 1, 2 (byte 0: low nibble first) and 7, 15
+    vals = mo.e2m1_to_f64(mo.unpack_e2m1(np.array([[0x21, 0xF7]], np.uint8)))
+    assert vals.tolist() == [[0.5, 1.0, 6.0, -6.0]]
+
+
+def test_generator_e2m1_rounds_to_nearest_even_and_saturates():
+    v = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 100.0, -0.25, -2.9, 0.26])
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0, 0.0, -3.0, 0.5]
+    assert mo.e2m1_to_f64(mi.e2m1_encode(v)).tolist() == want
+
+
+def test_mx_quantisation_error_bounds():
+    # the scale's exponent is floor(log2 amax) minus the element format's
+    # largest exponent, so a block's amax maps into [4, 8) for e2m1 and
+    # [256, 512) for e4m3: elements are within half a step of the draw, or
+    # clamped to the largest magnitude (6, resp. 448)
+    rng = np.random.default_rng(9)
+    a = (rng.standard_normal((64, 256)) * np.exp(rng.standard_normal((64, 1)) * 3)).astype(np.float32)
+    p, s = mi.quantize_mx_e2m1(a)
+    scale = np.repeat(mo.e8m0_to_f64(s), 32, axis=1)
+    dq = mo.dequant_mx(mo.e2m1_to_f64(mo.unpack_e2m1(p)), s)
+    amax = np.repeat(np.abs(a.reshape(64, 8, 32)).max(axis=2), 32, axis=1)
+    assert ((amax / scale >= 4) & (amax / scale < 8)).all()
+    err = np.abs(dq - a)
+    clamped = np.abs(a) / scale > 6
+    assert (err[~clamped] <= 1.0 * scale[~clamped] * (1 + 1e-9)).all()     # half of step 2 at [4, 6]
+    assert (err[clamped] <= 2.0 * scale[clamped]).all()
+    c, s8 = mi.quantize_mx_e4m3(a)
+    scale8 = np.repeat(mo.e8m0_to_f64(s8), 32, axis=1)
+    dq8 = mo.dequant_mx(mo.e4m3_to_f64(c), s8)
+    rel = np.abs(dq8 - a) / np.abs(a)
+    clamped8 = np.abs(a) / scale8 > 448
+    big = (np.abs(a) / scale8 >= 2.0 ** -6) & ~clamped8         # normal e4m3 range
+    assert (rel[big] <= 2.0 ** -4 * (1 + 1e-9)).all()
+    assert (np.abs(dq8 - a)[clamped8] <= 64 * scale8[clamped8]).all()
+
+
+def test_w4a8_oracle_uses_dequantized_inputs():
+    wl = mi.Workload("w4", 1, 4, 8, 2, 0, 2, 256, 128, "w4a8", False, 81)
+    inp = mi.make_inputs(wl)
+    r = mo.run(inp, block_m=16)
+    x = mo.e4m3_to_f64(inp.x) * np.kron(2.0 ** (inp.x_scale.astype(np.float64) - 127), np.ones(32))
+    C = np.zeros_like(r.C)
+    for n in range(4):
+        for j in range(2):
+            e = int(r.idx[n, j])
+            if e < 2:
+                def dq(p, s):
+                    codes = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[0], -1)
+                    return mo.e2m1_to_f64(codes) * np.kron(2.0 ** (s.astype(np.float64) - 127),
+                                                           np.ones(32))
+                W1, W2 = dq(inp.w1[e], inp.w1_scale[e]), dq(inp.w2[e], inp.w2_scale[e])
+                g, u = x[n] @ W1[:128].T, x[n] @ W1[128:].T
+                C[n, j] = r.w[n, j] * ((g / (1 + np.exp(-g)) * u) @ W2.T)
+    np.testing.assert_allclose(r.C, C, rtol=0, atol=1e-12 * np.abs(C).max())
+    pairs = np.nonzero(r.layout.pair_row >= 0)[0]
+    got = mo.row_outputs(inp, r.idx, r.w, pairs)
+    np.testing.assert_allclose(got, r.C.reshape(-1, 256)[pairs], rtol=0, atol=1e-13 * np.abs(C).max())
