@@ -32,31 +32,38 @@ import moe_inputs as mi  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-FFN_KERNELS = {"bf16": "moe_ffn_bf16", "fp8": "moe_ffn_fp8"}
+FFN_KERNELS = {"bf16": "moe_ffn_bf16", "fp8": "moe_ffn_fp8", "w4a8": "moe_ffn_w4a8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip", "w4a8": "ffn_w4a8.hip"}
+
+
+def kernel_source_hash(dtype: str) -> str:
+    """Hash of the sources one dtype's FFN kernel is built from (its own file,
+    the shared device helpers and the schedules)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_ffn_persistent_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.startswith("ffn") or name == "sched.hpp":
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in (KERNEL_SOURCES[dtype], "ffn_common.hpp", "sched.hpp"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
 def algorithmic_counts(wl, R: int, active: int):
     H, I = wl.hidden, wl.inter
     flops = 6.0 * H * I * R
-    sw = 1 if wl.dtype == "fp8" else 2
+    sw = {"bf16": 2.0, "fp8": 1.0, "w4a8": 0.5}[wl.dtype]     # bytes per weight element
+    sx = 2.0 if wl.dtype == "bf16" else 1.0                     # per x and h element
     weight_bytes = active * 3.0 * H * I * sw
-    x_bytes = R * H * sw
-    h_bytes = 2.0 * R * I * sw
+    x_bytes = R * H * sx
+    h_bytes = 2.0 * R * I * sx
     comb_bytes = R * H * 2.0
     scale_bytes = 0.0
     if wl.dtype == "fp8":
         scale_bytes = active * 3.0 * (H // 128) * (I // 128) * 4 + R * (H // 128) * 4 \
             + 2.0 * R * (I // 128) * 4
+    elif wl.dtype == "w4a8":     # one E8M0 byte per 32 elements
+        scale_bytes = active * 3.0 * H * I / 32 + R * H / 32 + 2.0 * R * I / 32
     return flops, weight_bytes + x_bytes + h_bytes + comb_bytes + scale_bytes, dict(
         weights=weight_bytes, x=x_bytes, h=h_bytes, combine=comb_bytes, scales=scale_bytes)
 
@@ -128,7 +135,7 @@ def main():
     logits = up(inp.logits)
     bias = None if inp.bias is None else up(inp.bias)
     x = up(inp.x.reshape(S, T, H))
-    xs = None if inp.x_scale is None else up(inp.x_scale.reshape(S, T, H // 128))
+    xs = None if inp.x_scale is None else up(inp.x_scale.reshape(S, T, -1))
     w1, w2 = up(inp.w1), up(inp.w2)
     w1s = None if inp.w1_scale is None else up(inp.w1_scale)
     w2s = None if inp.w2_scale is None else up(inp.w2_scale)
@@ -213,7 +220,8 @@ def main():
         torch.cuda.synchronize()
 
     plan = ffn.plan
-    peak_flops = PEAK_FP8_TFLOPS if wl.dtype == "fp8" else PEAK_BF16_TFLOPS
+    # W4A8 runs e2m1 x e4m3 MFMAs, which issue at the fp8 rate
+    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP8_TFLOPS
     ffn_avg_s = statistics.mean(ffn_ms) * 1e-3
     t_mfma = flops / (peak_flops * 1e12)
     t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
@@ -222,7 +230,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE)).get(wl.name)
-            if tr and tr.get("kernel_hash") == kernel_source_hash():
+            if tr and tr.get("kernel_hash") == kernel_source_hash(wl.dtype):
                 traffic = tr.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None
@@ -255,7 +263,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if wl.dtype == "fp8" else "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic (seeded normal inputs, random-init expert weights)",
         "config": {"workload": wl.name, "schedule": args.schedule, "slices": S,
                    "tokens_per_slice": T, "experts": wl.num_experts, "top_k": k,

@@ -56,7 +56,18 @@ typedef enum {
   MOE_ERR_TIMEOUT = -5,            /* device status: a dependency wait timed out */
 } moe_status;
 
-typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 } moe_dtype;
+/* Operand formats.
+ *   MOE_BF16      bf16 x and weights.
+ *   MOE_FP8_E4M3  OCP e4m3 x and weights with fp32 scales: one per 1x128
+ *                 block of x, one per 128x128 block of each weight matrix.
+ *   MOE_W4A8      OCP Microscaling (MX): weights e2m1 (4-bit, two per byte,
+ *                 element 2i in the low nibble of byte i), x e4m3, every
+ *                 block of 32 consecutive elements along K with one E8M0
+ *                 scale byte (2^(byte-127)). The X-Stage paper evaluates
+ *                 W4A8 and W8A8 (section 5.2.1) without naming the 4-bit
+ *                 format; MX is the format gfx950's matrix cores scale
+ *                 natively. */
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_W4A8 = 2 } moe_dtype;
 
 typedef enum { MOE_SCHED_EXPERT_WAVE = 0, MOE_SCHED_INTERLEAVED = 1 } moe_schedule;
 
@@ -179,14 +190,18 @@ int32_t moe_dispatch_layout(const moe_shape* shape, const float* logits,
 
 /* Persistent fused expert FFN (X-Stage paper, section 2.2 and Algorithm 1).
  *   x_slices       host array [S] of device pointers, each [T, H] of bf16
- *                  (MOE_BF16) or e4m3 bytes (MOE_FP8_E4M3).
- *   x_scales       fp8 only: host array [S] of device pointers, each
- *                  [T, H/128] fp32 (one scale per 1x128 block); else NULL.
+ *                  (MOE_BF16) or e4m3 bytes (MOE_FP8_E4M3, MOE_W4A8).
+ *   x_scales       host array [S] of device pointers, each [T, H/128] fp32
+ *                  (MOE_FP8_E4M3: one scale per 1x128 block) or [T, H/32]
+ *                  E8M0 bytes (MOE_W4A8); NULL for MOE_BF16.
  *   w1             [L, 2I, H]: rows 0..I-1 of expert e are the gate
- *                  projection, rows I..2I-1 the up projection.
- *   w1_scales      fp8 only: [L, 2I/128, H/128] fp32 per 128x128 block.
- *   w2             [L, H, I] down projection.
- *   w2_scales      fp8 only: [L, H/128, I/128] fp32.
+ *                  projection, rows I..2I-1 the up projection (MOE_W4A8:
+ *                  [L, 2I, H/2] bytes of packed e2m1).
+ *   w1_scales      MOE_FP8_E4M3: [L, 2I/128, H/128] fp32 per 128x128 block;
+ *                  MOE_W4A8: [L, 2I, H/32] E8M0 bytes; NULL for MOE_BF16.
+ *   w2             [L, H, I] down projection (MOE_W4A8: [L, H, I/2] bytes).
+ *   w2_scales      MOE_FP8_E4M3: [L, H/128, I/128] fp32; MOE_W4A8:
+ *                  [L, H, I/32] E8M0 bytes.
  *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
  *                  Slot (t, j) of slice s receives
  *                     bf16( w[n, j] * FFN_e(x[n]) ),  n = s*T + t,
@@ -197,9 +212,9 @@ int32_t moe_dispatch_layout(const moe_shape* shape, const float* logits,
  * The layout must come from moe_dispatch_layout with layout->block_m equal
  * to moe_ffn_plan().block_m for the same shape and parameters. */
 int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
-                        const void* const* x_slices, const float* const* x_scales,
-                        const void* w1, const float* w1_scales,
-                        const void* w2, const float* w2_scales,
+                        const void* const* x_slices, const void* const* x_scales,
+                        const void* w1, const void* w1_scales,
+                        const void* w2, const void* w2_scales,
                         void* const* combine_slices,
                         void* workspace, size_t workspace_bytes,
                         const moe_sched_params* params, void* stream);

@@ -13,14 +13,14 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import (MOE_BF16, MOE_FP8_E4M3, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED,
+from ._lib import (MOE_BF16, MOE_FP8_E4M3, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, MOE_W4A8,
                    MoeError, MoeLayout, MoePlan, MoeSchedParams, MoeShape)
 
 __all__ = ["MoeExpertFFN", "LayoutBuffers", "MoeError", "SCHEDULES", "make_shape",
            "make_params", "library"]
 
 SCHEDULES = {"expert_wave": MOE_SCHED_EXPERT_WAVE, "interleaved": MOE_SCHED_INTERLEAVED}
-DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "w4a8": MOE_W4A8}
 
 
 def library():
@@ -134,7 +134,8 @@ class MoeExpertFFN:
         sh = self.shape
         S, T, L, H, I, k = (sh.num_slices, sh.tokens_per_slice, sh.num_local_experts, sh.hidden,
                             sh.inter, sh.top_k)
-        elt = 1 if self.dtype == "fp8" else 2
+        elt = 2 if self.dtype == "bf16" else 1          # bytes per x element
+        wpe = {"bf16": 2.0, "fp8": 1.0, "w4a8": 0.5}[self.dtype]   # bytes per weight element
 
         def need(t, nbytes, what):
             if t is None:
@@ -153,14 +154,19 @@ class MoeExpertFFN:
         for t, n, what in ((w1, L * 2 * I * H, "w1"), (w2, L * H * I, "w2")):
             if t.element_size() != elt:
                 raise ValueError(f"{what} must have {elt}-byte elements for dtype {self.dtype}")
-            need(t, n * elt, what)
-        if self.dtype == "fp8":
+            need(t, int(n * wpe), what)
+        if self.dtype != "bf16":
             if x_scales is None or len(x_scales) != S:
-                raise ValueError("fp8 needs one x-scale tensor per slice")
+                raise ValueError(f"{self.dtype} needs one x-scale tensor per slice")
+            if self.dtype == "fp8":   # fp32 per 1x128 (x) and 128x128 (weights) block
+                xs_b, w1s_b, w2s_b = (T * (H // 128) * 4, L * (2 * I // 128) * (H // 128) * 4,
+                                      L * (H // 128) * (I // 128) * 4)
+            else:                     # one E8M0 byte per 1x32 block
+                xs_b, w1s_b, w2s_b = T * (H // 32), L * 2 * I * (H // 32), L * H * (I // 32)
             for t in x_scales:
-                need(t, T * (H // 128) * 4, "x scales")
-            need(w1_scales, L * (2 * I // 128) * (H // 128) * 4, "w1 scales")
-            need(w2_scales, L * (H // 128) * (I // 128) * 4, "w2 scales")
+                need(t, xs_b, "x scales")
+            need(w1_scales, w1s_b, "w1 scales")
+            need(w2_scales, w2s_b, "w2 scales")
 
     def forward(self, x_slices, w1, w2, combine_slices, x_scales=None, w1_scales=None,
                 w2_scales=None, stream=None, **sched):

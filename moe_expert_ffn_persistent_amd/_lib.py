@@ -18,6 +18,7 @@ MOE_ERR_TIMEOUT = -5
 
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
+MOE_W4A8 = 2
 MOE_SCHED_EXPERT_WAVE = 0
 MOE_SCHED_INTERLEAVED = 1
 MOE_MAX_SLICES = 64

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_ffn.so")
 ARCH = "gfx950"
 
-SOURCES = ["layout.hip", "ffn_bf16.hip", "ffn_fp8.hip", "combine.hip", "burst.hip", "api.cpp"]
+SOURCES = ["layout.hip", "ffn_bf16.hip", "ffn_fp8.hip", "ffn_w4a8.hip", "combine.hip", "burst.hip",
+           "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

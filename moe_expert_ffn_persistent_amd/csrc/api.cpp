@@ -22,6 +22,10 @@ extern const TileInfo kFp8Tiles[];
 extern const int kNumFp8Tiles;
 hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s);
 hipError_t occupancy_ffn_fp8(int id, int* n);
+extern const TileInfo kW4a8Tiles[];
+extern const int kNumW4a8Tiles;
+hipError_t launch_ffn_w4a8(int id, const FfnArgs& a, hipStream_t s);
+hipError_t occupancy_ffn_w4a8(int id, int* n);
 
 namespace {
 
@@ -59,6 +63,12 @@ int device_props(DeviceProps** out) {
       if (occupancy_ffn_fp8(id, &n) != hipSuccess) return MOE_ERR_HIP;
       p.occ[id] = n;
     }
+    for (int i = 0; i < kNumW4a8Tiles; ++i) {
+      int n = 0;
+      const int id = kW4a8Tiles[i].id;
+      if (occupancy_ffn_w4a8(id, &n) != hipSuccess) return MOE_ERR_HIP;
+      p.occ[id] = n;
+    }
     p.ready = true;
   }
   *out = &p;
@@ -75,7 +85,7 @@ bool shape_ok(const moe_shape* s) {
   if (s->local_expert_begin < 0 || s->local_expert_begin + s->num_local_experts > s->num_experts)
     return false;
   if (s->hidden < 128 || s->hidden % 128 || s->inter < 128 || s->inter % 128) return false;
-  if (s->dtype != MOE_BF16 && s->dtype != MOE_FP8_E4M3) return false;
+  if (s->dtype != MOE_BF16 && s->dtype != MOE_FP8_E4M3 && s->dtype != MOE_W4A8) return false;
   const long long pairs = (long long)s->num_slices * s->tokens_per_slice * s->top_k;
   if (pairs > (1ll << 30)) return false;
   return true;
@@ -88,6 +98,8 @@ const TileInfo* find_tile(int id) {
     if (kBf16Tiles[i].id == id) return &kBf16Tiles[i];
   for (int i = 0; i < kNumFp8Tiles; ++i)
     if (kFp8Tiles[i].id == id) return &kFp8Tiles[i];
+  for (int i = 0; i < kNumW4a8Tiles; ++i)
+    if (kW4a8Tiles[i].id == id) return &kW4a8Tiles[i];
   return nullptr;
 }
 
@@ -108,11 +120,13 @@ struct WsLayout {
 WsLayout carve(const moe_shape* s, int block_m, int max_rows) {
   WsLayout w{};
   const size_t rows = (size_t)max_rows * block_m;
-  const size_t elt = s->dtype == MOE_FP8_E4M3 ? 1 : 2;
+  const size_t elt = s->dtype == MOE_BF16 ? 2 : 1;
   w.h = 0;
   size_t off = align_up(rows * s->inter * elt, 256);
   w.hs = off;
+  // h scales: fp32 per 1x128 block (fp8), one E8M0 byte per 1x32 block (W4A8)
   if (s->dtype == MOE_FP8_E4M3) off = align_up(off + rows * (s->inter / 128) * 4, 256);
+  if (s->dtype == MOE_W4A8) off = align_up(off + rows * (s->inter / 32), 256);
   w.l2_full = off;
   off = align_up(off + (size_t)max_rows * 4, 256);
   w.done = off;
@@ -167,6 +181,10 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
   } else if (s->dtype == MOE_FP8_E4M3) {
     for (int i = 0; i < kNumFp8Tiles && !t; ++i)
       if (tile_fits(&kFp8Tiles[i], s)) t = &kFp8Tiles[i];
+    if (!t) return MOE_ERR_UNSUPPORTED;
+  } else if (s->dtype == MOE_W4A8) {
+    for (int i = 0; i < kNumW4a8Tiles && !t; ++i)
+      if (tile_fits(&kW4a8Tiles[i], s)) t = &kW4a8Tiles[i];
     if (!t) return MOE_ERR_UNSUPPORTED;
   } else {
     // expected rows per local expert under uniform routing; pick the
@@ -250,13 +268,13 @@ int32_t moe_dispatch_layout(const moe_shape* s, const float* logits, const float
 }
 
 int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* const* x_slices,
-                        const float* const* x_scales, const void* w1, const float* w1_scales,
-                        const void* w2, const float* w2_scales, void* const* comb, void* ws,
+                        const void* const* x_scales, const void* w1, const void* w1_scales,
+                        const void* w2, const void* w2_scales, void* const* comb, void* ws,
                         size_t ws_bytes, const moe_sched_params* prm, void* stream) {
   if (!shape_ok(s) || !lay || !prm || !x_slices || !comb || !w1 || !w2 || !ws)
     return MOE_ERR_INVALID_ARG;
-  const bool fp8 = s->dtype == MOE_FP8_E4M3;
-  if (fp8 && (!x_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  const bool scaled = s->dtype != MOE_BF16;   // fp8 and W4A8 carry block scales
+  if (scaled && (!x_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   moe_plan plan{};
   int st = moe_ffn_plan(s, prm, &plan);
   if (st != MOE_OK) return st;
@@ -267,7 +285,7 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   if (prm->trace && prm->trace_capacity < 1) return MOE_ERR_INVALID_ARG;
   if (num_tokens(s) == 0) return MOE_OK;
   for (int i = 0; i < s->num_slices; ++i)
-    if (!x_slices[i] || !comb[i] || (fp8 && !x_scales[i])) return MOE_ERR_INVALID_ARG;
+    if (!x_slices[i] || !comb[i] || (scaled && !x_scales[i])) return MOE_ERR_INVALID_ARG;
   DeviceProps* dp = nullptr;
   st = device_props(&dp);
   if (st != MOE_OK) return st;
@@ -300,13 +318,13 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   a.timeout_ticks = (long long)(prm->timeout_ms > 0 ? prm->timeout_ms : 2000) * dp->wall_khz;
   for (int i = 0; i < s->num_slices; ++i) {
     a.x[i] = x_slices[i];
-    a.xs[i] = x_scales ? x_scales[i] : nullptr;
+    a.xs[i] = x_scales ? static_cast<const float*>(x_scales[i]) : nullptr;
     a.comb[i] = comb[i];
   }
   a.w1 = w1;
-  a.w1s = w1_scales;
+  a.w1s = static_cast<const float*>(w1_scales);
   a.w2 = w2;
-  a.w2s = w2_scales;
+  a.w2s = static_cast<const float*>(w2_scales);
   a.row_offset = lay->row_offset;
   a.tile_offset = lay->tile_offset;
   a.row_pair = lay->row_pair;
@@ -318,8 +336,9 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
   a.done = reinterpret_cast<int32_t*>(base + w.done);
   a.status = prm->status;
   a.trace = prm->trace;
-  const hipError_t err = fp8 ? launch_ffn_fp8(plan.tile, a, (hipStream_t)stream)
-                             : launch_ffn_bf16(plan.tile, a, (hipStream_t)stream);
+  const hipError_t err = s->dtype == MOE_FP8_E4M3 ? launch_ffn_fp8(plan.tile, a, (hipStream_t)stream)
+                         : s->dtype == MOE_W4A8   ? launch_ffn_w4a8(plan.tile, a, (hipStream_t)stream)
+                                                  : launch_ffn_bf16(plan.tile, a, (hipStream_t)stream);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

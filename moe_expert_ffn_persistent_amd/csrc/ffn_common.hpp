@@ -104,15 +104,22 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // 16-byte store with a cache policy (inline assembly: completion is awaited
 // with vm_wait like the copies). kCoherent: device scope (sc1), written
 // through this XCD's L2; kStream: non-temporal.
+//
+// A store of more than 8 bytes reads its data registers after it issues, so
+// the next instruction must not overwrite them (one wait state on this GPU
+// family). The compiler inserts that wait for its own stores but cannot see
+// into inline assembly, and does reuse the data registers right away (seen
+// as the loop counter landing in the first four bytes of some rows); the
+// s_nop inside the statement keeps the wait.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <int POL>
 __device__ __forceinline__ void store16(void* dst, i32x4 v) {
   if constexpr (POL == kCoherent)
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
   else if constexpr (POL == kStream)
-    asm volatile("global_store_dwordx4 %0, %1, off nt" ::"v"(dst), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
   else
-    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
 }
 
 // Trace of an epilogue's stores (`tracing` uniform over the workgroup, `rec`
@@ -154,6 +161,21 @@ __device__ __forceinline__ void dma4(const char* src, uint32_t m0) {
   else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0)
                  : "memory", "m0");
+}
+
+// e4m3 (OCP fp8) codes of four values, round to nearest even
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// e4m3 code of clamp(h * inv, +-448) for four values, round to nearest even
+__device__ __forceinline__ uint32_t quant4(const float (&h)[4], float inv) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[i] * inv, -448.f), 448.f);
+  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
 }
 
 // Routed pair and router weight of each row of a Linear-2 tile, copied to

@@ -71,20 +71,6 @@ struct Cfg8 {
 
 constexpr int kMaxKBlocks = 128;   // H/128 and I/128 limit
 
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
-// e4m3 code of clamp(h * inv, +-448) for four values, round to nearest even
-__device__ __forceinline__ uint32_t quant4(const float (&h)[4], float inv) {
-  float q[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[i] * inv, -448.f), 448.f);
-  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
-}
-
 // Operand and token-scale copies, shared by both fp8 tiles.
 template <class C>
 struct Tile8Copies {

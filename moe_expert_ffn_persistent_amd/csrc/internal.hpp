@@ -63,10 +63,10 @@ struct FfnArgs {
   int trace_cap;
   long long timeout_ticks; // wall-clock ticks before a wait gives up
   const void* x[MOE_MAX_SLICES];
-  const float* xs[MOE_MAX_SLICES];
+  const float* xs[MOE_MAX_SLICES];   // fp8: fp32 1x128 scales; W4A8: E8M0 bytes per 1x32
   void* comb[MOE_MAX_SLICES];
   const void* w1;
-  const float* w1s;
+  const float* w1s;        // fp8: fp32 128x128 scales; W4A8: E8M0 bytes per 1x32
   const void* w2;
   const float* w2s;
   const int32_t* row_offset;
@@ -74,7 +74,8 @@ struct FfnArgs {
   const int32_t* row_pair;
   const float* row_weight;
   void* h;                 // [P_cap * block_m, I] intermediate activations
-  float* hs;               // fp8: [P_cap * block_m, I/128] scales
+  float* hs;               // fp8: [P_cap * block_m, I/128] fp32 scales; W4A8:
+                           // [P_cap * block_m, I/32] E8M0 bytes
   int32_t* l2_full;        // [P_cap] finished Linear-1 tiles per row
   int32_t* done;           // [1] finished workgroups
   int32_t* status;         // device status word or nullptr

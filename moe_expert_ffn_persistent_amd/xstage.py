@@ -319,7 +319,7 @@ def ffn_spans(workload: str = "dsv3") -> dict:
     S, T, H, k = wl.num_slices, wl.tokens_per_slice, wl.hidden, wl.top_k
     up = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
     x = up(inp.x.reshape(S, T, H))
-    xs = None if inp.x_scale is None else up(inp.x_scale.reshape(S, T, H // 128))
+    xs = None if inp.x_scale is None else up(inp.x_scale.reshape(S, T, -1))
     w1, w2 = up(inp.w1), up(inp.w2)
     w1s = None if inp.w1_scale is None else up(inp.w1_scale)
     w2s = None if inp.w2_scale is None else up(inp.w2_scale)

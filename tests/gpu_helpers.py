@@ -35,7 +35,7 @@ class Uploaded:
             self.x_slices = [self.x_all[s] for s in range(S)]
         self.x_scales = None
         if inp.x_scale is not None:
-            xs = inp.x_scale.reshape(S, T, H // 128)
+            xs = inp.x_scale.reshape(S, T, -1)
             self.xs_all = to_dev(xs)
             self.x_scales = [self.xs_all[s] for s in range(S)]
         self.w1 = to_dev(inp.w1)
