@@ -33,7 +33,7 @@ def _check_layout(wl, lb, idx_ref, w_ref, block_m, routed=True):
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsv3", "dsv3_skew", "qwen3_decode", "qwen3_prefill",
-                                  "dsv3_fp8"])
+                                  "dsv3_fp8", "dsv3_w4a8"])
 def test_routing_and_layout_match_oracle(name):
     wl = mi.get_workload(name)
     if wl.dtype == "fp8":
