@@ -451,7 +451,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_w4a8(const FfnArgs a) {
 }
 
 // CfgMx<tokens, features, token waves, feature waves, ring stages, copy spread>
-using CfgMxMain = CfgMx<192, 256, 2, 4, 3, 2>;   // 96 tokens x 64 features per wavefront
+using CfgMxMain = CfgMx<192, 256, 2, 4, 3, 6>;   // 96 tokens x 64 features per wavefront
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
