@@ -13,8 +13,12 @@
 //    the whole K block, and each block is promoted right behind the matrix
 //    core, which keeps the register budget of a 192 x 256 tile within eight
 //    wavefronts (fewer copy bytes per FLOP than 128 x 256).
-//  - Token scales of the stage are copied into LDS next to the operands by
-//    four-byte direct-to-LDS copies; the weight scales of the task (two
+//  - Weight rows and token rows sit in two LDS rings. The default tile gives
+//    the weights one stage more than the tokens (three against two, which
+//    is what 160 KiB holds at 192 x 256): a weight stage is copied two
+//    stages ahead, a token stage one stage ahead.
+//  - Token scales of the stage are copied into LDS next to the token rows
+//    by four-byte direct-to-LDS copies; the weight scales of the task (two
 //    128-row blocks) are staged in LDS once per task.
 //  - Linear-1 writes h as e4m3 with one fp32 scale per token and 128 columns
 //    (amax/448, values clamped to +-448, round to nearest even): a 256-wide
@@ -31,9 +35,14 @@
 namespace moe {
 namespace {
 
-template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false, int SP_ = MOE_ISSUE_SPREAD>
+template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false, int SP_ = MOE_ISSUE_SPREAD,
+          int XW_ = 0>
 struct Cfg8 {
   static constexpr int TM = TM_, TN = TN_, WT = WT_, WF = WF_, NS = NS_;
+  // ring depths: NS token stages and NS + XW weight stages (XW = 1: a
+  // weight stage is copied two stages ahead, a token stage one stage ahead)
+  static constexpr int XW = XW_, NST = NS, NSW = NS + XW;
+  static_assert(XW == 0 || XW == 1, "weight ring at most one stage deeper");
   // WIDE: 16x16x128 MFMAs (one per output block and K block), promoted
   // block by block between them (Tile8W); else 32x32x64 MFMAs (Tile8)
   static constexpr bool WIDE = WIDE_;
@@ -46,11 +55,23 @@ struct Cfg8 {
   static constexpr int NID = (TN + TM) / RPI / NW;      // operand copies per wavefront per stage
   static constexpr int NIW = TN / RPI / NW;             // of which weight rows (the first NIW)
   static constexpr int NI = NID + 1;                    // plus one token-scale copy
-  static constexpr int A_BYTES = TN * ROW_BYTES;
-  // token scales: wavefront w copies the scales of rows (64w + lane) mod TM
-  // into its own 256-byte slot, so row q's scale sits at word q
-  static constexpr int SCALE_OFF = (TN + TM) * ROW_BYTES;
-  static constexpr int STAGE_BYTES = SCALE_OFF + NW * 256;
+  static constexpr int NTC = NI - NIW;                  // token-row and token-scale copies
+  // LDS: NSW weight stages of TN rows, then NST token stages of TM rows and
+  // the token scales (wavefront w copies the scales of rows (64w + lane) mod
+  // TM into its own 256-byte slot, so row q's scale sits at word q)
+  static constexpr int W_BYTES = TN * ROW_BYTES;
+  static constexpr int SCALE_OFF = TM * ROW_BYTES;      // within a token stage
+  static constexpr int T_BYTES = SCALE_OFF + NW * 256;
+  static constexpr int T_RING = NSW * W_BYTES;
+  static constexpr int LDS_BYTES = T_RING + NST * T_BYTES;
+  static constexpr uint32_t w_off(int s) { return s * W_BYTES; }
+  static constexpr uint32_t t_off(int s) { return T_RING + s * T_BYTES; }
+  // copy issued o-th in a stage: with a deeper weight ring the token copies
+  // (awaited one stage later) go first, since copies complete in issue order
+  static constexpr int copy_of(int o) { return XW == 0 ? o : (o < NTC ? NIW + o : o - NTC); }
+  // copies still in flight when a stage's operands have landed: the weights
+  // of the stage after next (XW = 1), the stages after next (NS > 2)
+  static constexpr int WAIT = (XW ? NIW : 0) + NI * (NST - 2);
   // MFMAs per wavefront per stage: one 16x16x128 per 16 x 16 block (WIDE), or
   // two 32x32x64 per 32 x 32 block
   static constexpr int NM = WIDE ? (FT / 16) * (TT / 16) : 2 * FB * TB;
@@ -66,7 +87,8 @@ struct Cfg8 {
   static_assert(TT % 32 == 0 && FT % 32 == 0 && FB % 2 == 0, "wavefront tile");
   static_assert(((TN + TM) / RPI) % NW == 0, "copies split evenly");
   static_assert(TN % (RPI * NW) == 0, "every wavefront copies weight rows in its first NIW instructions");
-  static_assert(NS >= 2 && NI * (NS - 1) <= 63, "vmcnt range");
+  static_assert(NS >= 2 && NI * NSW <= 63, "vmcnt range");
+  static_assert(W_BYTES % 1024 == 0 && T_BYTES % 1024 == 0, "1 KiB copy slots");
 };
 
 constexpr int kMaxKBlocks = 128;   // H/128 and I/128 limit
@@ -93,25 +115,43 @@ struct Tile8Copies {
     ssrc = srow((wave * 64 + lane) % C::TM);
   }
 
-  // copy i of stage kt into the ring slot at LDS address `slot`: operand
-  // rows (weights first), then the token scales
+  // copy i: weight rows of K block ktw into the weight slot at LDS address
+  // wslot (i < NIW), token rows of K block ktt (i < NID) or their scales
+  // into the token slot at tslot
   template <bool COH>
-  __device__ __forceinline__ void issue_one(int i, int kt, uint32_t slot) {
+  __device__ __forceinline__ void issue_one(int i, int ktw, int ktt, uint32_t wslot, uint32_t tslot) {
     const int wave = threadIdx.x >> 6;
-    if (i < C::NID) {
-      const uint32_t dst = uni(slot + (wave + C::NW * i) * 1024);
-      const char* sp = src[i] + (size_t)kt * C::ROW_BYTES;
-      if (i < C::NIW) dma16<MOE_WEIGHT_POLICY>(sp, dst);
-      else if (COH) dma16<kCoherent>(sp, dst);
+    if (i < C::NIW) {
+      dma16<MOE_WEIGHT_POLICY>(src[i] + (size_t)ktw * C::ROW_BYTES, uni(wslot + (wave + C::NW * i) * 1024));
+    } else if (i < C::NID) {
+      const uint32_t dst = uni(tslot + (wave + C::NW * (i - C::NIW)) * 1024);
+      const char* sp = src[i] + (size_t)ktt * C::ROW_BYTES;
+      if (COH) dma16<kCoherent>(sp, dst);
       else dma16<kCacheNormal>(sp, dst);
     } else {
-      const uint32_t dst = uni(slot + C::SCALE_OFF + wave * 256);
-      if (COH) dma4<kCoherent>(ssrc + kt * 4, dst);
-      else dma4<kCacheNormal>(ssrc + kt * 4, dst);
+      const uint32_t dst = uni(tslot + C::SCALE_OFF + wave * 256);
+      if (COH) dma4<kCoherent>(ssrc + ktt * 4, dst);
+      else dma4<kCacheNormal>(ssrc + ktt * 4, dst);
     }
   }
 
-  // 32 bytes of 128-byte row r of the stage at logical 16-byte chunks c, c+1
+  // Where the copies of the stage being computed go: the K blocks and LDS
+  // slots of the token and weight stages they fill.
+  struct Next {
+    int ktw, ktt;
+    uint32_t wslot, tslot;
+  };
+
+  // the copy issued o-th in a stage
+  template <bool COH>
+  __device__ __forceinline__ void issue_nth(int o, const Next& nx) {
+    issue_one<COH>(C::copy_of(o), nx.ktw, nx.ktt, nx.wslot, nx.tslot);
+  }
+
+  // 32 bytes of 128-byte row r of a weight or token stage at logical 16-byte
+  // chunks c, c+1 (the XOR swizzle of the copy: TN is a multiple of 16, so a
+  // token row's swizzle is the same whether counted from the weight rows or
+  // from its own stage)
   __device__ __forceinline__ static i32x8 frag32(const char* stage, int r, int c) {
     const int swz = (r >> 1) & 7;
     const char* row = stage + r * C::ROW_BYTES;
@@ -120,32 +160,42 @@ struct Tile8Copies {
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 
-  // K loop over nk 128-wide blocks through the NS-stage ring: stage kt is
+  // K loop over nk 128-wide blocks through the two rings: stage kt is
   // awaited (own copies, then one workgroup barrier), then multiplied (by the
-  // tile's compute) while the copy of stage kt+NS-1 goes into the slot stage
-  // kt-1 used. The copy is issued unconditionally (the last NS-1 stages
-  // re-copy stage nk-1 into their free slot), so no branch splits the MFMA
-  // sequence it is spread over; those extra copies are awaited at the end,
-  // before the epilogue reuses LDS.
+  // tile's compute) while the token rows of stage kt+NST-1 and the weight
+  // rows of stage kt+NSW-1 go into the slots stage kt-1 used. The copies are
+  // issued unconditionally (the last stages re-copy stage nk-1 into their
+  // free slots), so no branch splits the MFMA sequence they are spread over;
+  // those extra copies are awaited at the end, before the epilogue reuses LDS.
+  // The prologue issues what the stages before stage 0 would have, in the
+  // same order, so that one wait count holds for every stage.
   template <bool COH, class Tile>
   __device__ __forceinline__ void kloop(Tile& t, char* lds, int nk, int wf, int wt, const float* sw,
                                         bool l1) {
     lds_barrier();
 #pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s) {
-      const int ks = min(s, nk - 1);
+    for (int v = 1 - C::NSW; v < 0; ++v) {
+      const int st = v + C::NST - 1, sw_ = v + C::NSW - 1;
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, ks, ring + s * C::STAGE_BYTES);
+      for (int o = 0; o < C::NI; ++o) {
+        const int i = C::copy_of(o);
+        if (i < C::NIW ? sw_ < 0 : st < 0) continue;
+        issue_one<COH>(i, min(sw_, nk - 1), min(st, nk - 1), ring + C::w_off(sw_ < 0 ? 0 : sw_),
+                       ring + C::t_off(st < 0 ? 0 : st));
+      }
     }
-    int slot = 0;
+    int ws = 0, ts = 0;   // slots of stage kt
     for (int kt = 0; kt < nk; ++kt) {
-      vm_wait<C::NI * (C::NS - 2)>();   // stage kt has landed (later stages may not have)
+      vm_wait<C::WAIT>();   // stage kt has landed (later stages may not have)
       lds_barrier();
-      const int nxt = min(kt + C::NS - 1, nk - 1);
-      const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      t.template compute<COH>(lds + slot * C::STAGE_BYTES, wf, wt, kt, sw, l1, nxt,
-                              ring + nslot * C::STAGE_BYTES);
-      slot = slot + 1 == C::NS ? 0 : slot + 1;
+      Next nx;
+      nx.ktt = min(kt + C::NST - 1, nk - 1);
+      nx.ktw = min(kt + C::NSW - 1, nk - 1);
+      nx.tslot = ring + C::t_off(ts == 0 ? C::NST - 1 : ts - 1);
+      nx.wslot = ring + C::w_off(ws == 0 ? C::NSW - 1 : ws - 1);
+      t.template compute<COH>(lds + C::w_off(ws), lds + C::t_off(ts), wf, wt, kt, sw, l1, nx);
+      ws = ws + 1 == C::NSW ? 0 : ws + 1;
+      ts = ts + 1 == C::NST ? 0 : ts + 1;
     }
     vm_wait<0>();
   }
@@ -162,12 +212,12 @@ struct Tile8 : Tile8Copies<C> {
 
   // fragment q (q < FB: weights, else tokens) of MFMA step mi: 32 K-elements
   // per lane
-  __device__ __forceinline__ void load_frag(const char* stage, int mi, int q, int wf, int wt,
+  __device__ __forceinline__ void load_frag(const char* wst, const char* tst, int mi, int q, int wf, int wt,
                                             i32x8 (&af)[C::FB], i32x8 (&bf)[C::TB]) {
     const int lane = threadIdx.x & 63;
     const int c0 = 4 * mi + 2 * (lane >> 5);
-    if (q < C::FB) af[q] = this->frag32(stage, wf * C::FT + q * 32 + (lane & 31), c0);
-    else bf[q - C::FB] = this->frag32(stage, C::TN + wt * C::TT + (q - C::FB) * 32 + (lane & 31), c0);
+    if (q < C::FB) af[q] = this->frag32(wst, wf * C::FT + q * 32 + (lane & 31), c0);
+    else bf[q - C::FB] = this->frag32(tst, wt * C::TT + (q - C::FB) * 32 + (lane & 31), c0);
   }
 
   // acc += part * (token scale x weight scale of K block kb), per output block
@@ -192,14 +242,14 @@ struct Tile8 : Tile8Copies<C> {
   // between MFMAs and VALU promotion after every workgroup barrier rather
   // than promoting together.
   template <bool COH>
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
-                                          bool l1, int kt_next, uint32_t slot) {
+  __device__ __forceinline__ void compute(const char* wst, const char* tst, int wf, int wt, int kt,
+                                          const float* sw, bool l1, const typename Tile8Copies<C>::Next& nx) {
     constexpr int NMF = C::FB * C::TB;
     constexpr int NL = C::FB + C::TB;
     const int r_lane = threadIdx.x & 31;
     i32x8 af[2][C::FB], bf[2][C::TB];
 #pragma unroll
-    for (int q = 0; q < NL; ++q) load_frag(stage, 0, q, wf, wt, af[0], bf[0]);
+    for (int q = 0; q < NL; ++q) load_frag(wst, tst, 0, q, wf, wt, af[0], bf[0]);
     if (lag && kt > 0) promote(st_prev, kt - 1, wf, sw, l1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -214,17 +264,17 @@ struct Tile8 : Tile8Copies<C> {
           // the second step's fragments (after the last first-step MFMA with
           // eight wavefronts, so that the two fragment sets share registers)
 #pragma unroll
-          for (int q = 0; q < NL; ++q) load_frag(stage, 1, q, wf, wt, af[1], bf[1]);
+          for (int q = 0; q < NL; ++q) load_frag(wst, tst, 1, q, wf, wt, af[1], bf[1]);
         }
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
-          if (C::issue_slot(i) == mi * NMF + m) this->template issue_one<COH>(i, kt_next, slot);
+          if (C::issue_slot(i) == mi * NMF + m) this->template issue_nth<COH>(i, nx);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // this stage's token scales; a lagging wavefront keeps them for the next
     // stage (the slot is refilled only by a copy issued during the next stage)
-    const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
+    const float* sx = reinterpret_cast<const float*>(tst + C::SCALE_OFF);
     float st[C::TB];
 #pragma unroll
     for (int tb = 0; tb < C::TB; ++tb) st[tb] = sx[wt * C::TT + tb * 32 + r_lane];
@@ -363,8 +413,8 @@ struct Tile8W : Tile8Copies<C> {
   float s_tail[2];
 
   template <bool COH>
-  __device__ __forceinline__ void compute(const char* stage, int wf, int wt, int kt, const float* sw,
-                                          bool l1, int kt_next, uint32_t slot) {
+  __device__ __forceinline__ void compute(const char* wst, const char* tst, int wf, int wt, int kt,
+                                          const float* sw, bool l1, const typename Tile8Copies<C>::Next& nx) {
     const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, c0 = 2 * (lane >> 4);
     i32x8 af[FB16], bf[2];
@@ -372,9 +422,9 @@ struct Tile8W : Tile8Copies<C> {
     // reads LDS at once after the stage barrier, and LDS reads complete in
     // order, so the remaining weight fragments are read one per MFMA, ahead
     // of the MFMA that needs them, instead of holding up the first one.
-    bf[0] = this->frag32(stage, C::TN + wt * C::TT + r16, c0);
-    af[0] = this->frag32(stage, wf * C::FT + r16, c0);
-    const float* sx = reinterpret_cast<const float*>(stage + C::SCALE_OFF);
+    bf[0] = this->frag32(tst, wt * C::TT + r16, c0);
+    af[0] = this->frag32(wst, wf * C::FT + r16, c0);
+    const float* sx = reinterpret_cast<const float*>(tst + C::SCALE_OFF);
     float swv[FB16];
 #pragma unroll
     for (int i = 0; i < FB16; ++i) swv[i] = block_scale(sw, kt, wf, i, l1);
@@ -384,11 +434,11 @@ struct Tile8W : Tile8Copies<C> {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int j = b / FB16, i = b % FB16;   // token block, feature block
-      if (b + 1 < FB16) af[b + 1] = this->frag32(stage, wf * C::FT + (b + 1) * 16 + r16, c0);
+      if (b + 1 < FB16) af[b + 1] = this->frag32(wst, wf * C::FT + (b + 1) * 16 + r16, c0);
       // next token block: its fragment once this block's first MFMA is out,
       // its scale once the promotions of the block before it are done
       if (i == 0 && j + 1 < TB16)
-        bf[(j + 1) & 1] = this->frag32(stage, C::TN + wt * C::TT + (j + 1) * 16 + r16, c0);
+        bf[(j + 1) & 1] = this->frag32(tst, wt * C::TT + (j + 1) * 16 + r16, c0);
       if (i == FB16 / 2 && j + 1 < TB16) stj[(j + 1) & 1] = sx[wt * C::TT + (j + 1) * 16 + r16];
       // formats 0/0: e4m3 x e4m3; E8M0 scales 127 = 2^0
       part[b % NP] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j & 1], f32x4{}, 0, 0, 0, 127,
@@ -407,7 +457,7 @@ struct Tile8W : Tile8Copies<C> {
       }
 #pragma unroll
       for (int k = 0; k < C::NI; ++k)
-        if (C::issue_slot(k) == b) this->template issue_one<COH>(k, kt_next, slot);
+        if (C::issue_slot(k) == b) this->template issue_nth<COH>(k, nx);
       __builtin_amdgcn_sched_barrier(0);
     }
     s_tail[0] = stj[(TB16 - 1) & 1] * swv[FB16 - 2];
@@ -443,7 +493,7 @@ struct Tile8W : Tile8Copies<C> {
     const int wf = wave % C::WF, wt = wave / C::WF;
     const int r16 = lane & 15;
     constexpr int HROW = C::TN / 2;   // the N-tile's h columns, one byte each
-    static_assert(C::TM * HROW <= C::NS * C::STAGE_BYTES, "h staging fits the ring");
+    static_assert(C::TM * HROW <= C::LDS_BYTES, "h staging fits the ring");
     float hv[TB16][2][4];
 #pragma unroll
     for (int j = 0; j < TB16; ++j) {
@@ -500,7 +550,7 @@ struct Tile8W : Tile8Copies<C> {
     const int wf = wave % C::WF, wt = wave / C::WF;
     const int r16 = lane & 15;
     constexpr int CROW = C::TN * 2;   // bf16 combine row piece of the N-tile
-    static_assert(C::TM * CROW + C::TM * (int)sizeof(char*) <= C::NS * C::STAGE_BYTES,
+    static_assert(C::TM * CROW + C::TM * (int)sizeof(char*) <= C::LDS_BYTES,
                   "combine staging and row destinations fit the ring");
     char** const rowdst = reinterpret_cast<char**>(lds + C::TM * CROW);
     const int rows = min(C::TM, Me - m * C::TM);   // padding rows are never stored
@@ -549,7 +599,7 @@ struct Meta8 {
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_fp8(const FfnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[C::NS * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
   __shared__ Meta8 meta8;
   __shared__ float amax_s[C::NW * C::TT];   // per-token h amax of each wavefront
   __shared__ int pair_s[C::TM];             // routed pair and router weight of each row of a
@@ -716,6 +766,10 @@ using Cfg8Main = Cfg8<128, 256, 2, 2, 3>;   // 128 features x 64 tokens per wave
 using Cfg8W8 = Cfg8<128, 256, 2, 4, 3>;     // 64 x 64 per wavefront, two wavefronts per SIMD
 using Cfg8Wide = Cfg8<192, 256, 2, 4, 2, true, 2>;   // 64 features x 96 tokens per wavefront, 16x16x128
 using Cfg8Wide3 = Cfg8<128, 256, 2, 4, 3, true>;  // 64 x 64 per wavefront, 16x16x128, three stages
+// as Cfg8Wide with a three-stage weight ring beside the two-stage token ring
+// (a weight stage is copied two stages ahead), copies spread over the whole
+// stage
+using Cfg8WideS = Cfg8<192, 256, 2, 4, 2, true, 8, 1>;
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -733,7 +787,8 @@ hipError_t occupancy(int* n) {
 extern const TileInfo kFp8Tiles[];
 extern const int kNumFp8Tiles;
 const TileInfo kFp8Tiles[] = {
-    {23, MOE_FP8_E4M3, Cfg8Wide::TM, Cfg8Wide::TN, Cfg8Wide::THREADS},   // first fitting tile is the default
+    {25, MOE_FP8_E4M3, Cfg8WideS::TM, Cfg8WideS::TN, Cfg8WideS::THREADS},   // first fitting tile is the default
+    {23, MOE_FP8_E4M3, Cfg8Wide::TM, Cfg8Wide::TN, Cfg8Wide::THREADS},
     {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},
     {24, MOE_FP8_E4M3, Cfg8Wide3::TM, Cfg8Wide3::TN, Cfg8Wide3::THREADS},
     {21, MOE_FP8_E4M3, Cfg8Main::TM, Cfg8Main::TN, Cfg8Main::THREADS},
@@ -746,6 +801,7 @@ hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
     case 22: return launch<Cfg8W8>(a, s);
     case 23: return launch<Cfg8Wide>(a, s);
     case 24: return launch<Cfg8Wide3>(a, s);
+    case 25: return launch<Cfg8WideS>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -756,6 +812,7 @@ hipError_t occupancy_ffn_fp8(int id, int* n) {
     case 22: return occupancy<Cfg8W8>(n);
     case 23: return occupancy<Cfg8Wide>(n);
     case 24: return occupancy<Cfg8Wide3>(n);
+    case 25: return occupancy<Cfg8WideS>(n);
   }
   return hipErrorInvalidValue;
 }
