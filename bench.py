@@ -8,9 +8,11 @@ y_local). Inputs are resident in HBM before the timed region starts.
 
 Prints one JSON line. ``value`` is TFLOP/s of the algorithmic FLOPs
 (6*H*I per routed row) over the whole step, for the schedule named in
-config.schedule; per-schedule FFN-only timings (paired, A-B-B-A order) and
-the roofline of the dominant kernel ride along, with the CPU oracle timed on
-a bounded sample of the same workload.
+config.schedule; per-schedule FFN-only timings (paired, A-B-C-C-B-A order,
+for Expert-Wave, Interleaved and the schedule planner's recommendation, with
+the planner's predictions beside them) and the roofline of the dominant
+kernel ride along, with the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -103,7 +105,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3", choices=sorted(mi.WORKLOADS))
-    ap.add_argument("--schedule", default="interleaved", choices=["interleaved", "expert_wave"])
+    ap.add_argument("--schedule", default="interleaved", choices=["interleaved", "expert_wave", "auto"],
+                    help="auto: the schedule planner's recommendation for the workload's routing, "
+                         "resolved once before the timed region")
     ap.add_argument("--pairs", type=int, default=10, help="A-B-B-A rounds of the schedule comparison")
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--lead-d", type=int, default=0)
@@ -150,15 +154,14 @@ def main():
                        lead_d=args.lead_d, device=dev)
     stream = torch.cuda.current_stream()
 
-    def ffn_call(schedule):
-        ffn.forward(x_sl, w1, w2, c_sl, x_scales=xs_sl, w1_scales=w1s, w2_scales=w2s,
-                    schedule=schedule)
+    def ffn_call(cfg):
+        ffn.forward(x_sl, w1, w2, c_sl, x_scales=xs_sl, w1_scales=w1s, w2_scales=w2s, **cfg)
 
-    def step(schedule, ev=None):
+    def step(cfg, ev=None):
         ffn.layout(logits=logits, bias=bias)
         if ev is not None:
             ev[0].record(stream)
-        ffn_call(schedule)
+        ffn_call(cfg)
         if ev is not None:
             ev[1].record(stream)
         ffn.combine_check(c_sl, y=y)
@@ -168,9 +171,15 @@ def main():
     totals = ffn.layout_bufs.totals.cpu().numpy()
     R, P, max_rows, active = (int(v) for v in totals)
     flops, alg_bytes, byte_parts = algorithmic_counts(wl, R, active)
+    # schedule planner for this routing (host model; reads the layout's counts)
+    pred = ffn.predict_schedule(schedule="interleaved", lead_d=args.lead_d)
+    rec = pred["recommended"]
+    rec_cfg = {"schedule": rec["schedule"], "lead_d": rec["lead_d"],
+               "experts_per_wave": rec["experts_per_wave"]}
+    head_cfg = rec_cfg if args.schedule == "auto" else {"schedule": args.schedule}
 
     for _ in range(args.warmup):
-        step(args.schedule)
+        step(head_cfg)
     torch.cuda.synchronize()
     if int(ffn.status.item()) != 0:
         raise RuntimeError(f"device status {int(ffn.status.item())} after warm-up")
@@ -181,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.schedule, evs[i])
+        step(head_cfg, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ffn_ms = [a.elapsed_time(b) for a, b in evs]
@@ -189,18 +198,21 @@ def main():
     if int(ffn.status.item()) != 0:
         raise RuntimeError(f"device status {int(ffn.status.item())} in the timed region")
 
-    # ---- paired schedule comparison, FFN only, A-B-B-A ----
-    per = {"expert_wave": [], "interleaved": []}
-    order = ["expert_wave", "interleaved"]
+    # ---- paired schedule comparison, FFN only, A-B-C-C-B-A: both orders
+    # with their default parameters, and the planner's recommendation ----
+    arms = {"expert_wave": {"schedule": "expert_wave"}, "interleaved": {"schedule": "interleaved"},
+            "recommended": rec_cfg}
+    per = {a: [] for a in arms}
+    order = list(arms)
     for r in range(args.pairs):
         seq = order if r % 2 == 0 else order[::-1]
-        for sched in seq:
+        for arm in seq:
             a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a_.record(stream)
-            ffn_call(sched)
+            ffn_call(arms[arm])
             b_.record(stream)
             b_.synchronize()
-            per[sched].append(a_.elapsed_time(b_))
+            per[arm].append(a_.elapsed_time(b_))
     sched_out = {}
     for s_, v in per.items():
         if not v:
@@ -265,7 +277,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded normal inputs, random-init expert weights)",
-        "config": {"workload": wl.name, "schedule": args.schedule, "slices": S,
+        "config": {"workload": wl.name, "schedule": args.schedule, "schedule_config": head_cfg, "slices": S,
                    "tokens_per_slice": T, "experts": wl.num_experts, "top_k": k,
                    "local_experts": wl.num_local, "hidden": H, "inter": wl.inter,
                    "routed_rows": R, "sched_rows": P, "max_rows_per_expert": max_rows,
@@ -276,6 +288,19 @@ def main():
         "ffn_only_ms": round(statistics.mean(ffn_ms), 4),
         "per_schedule": sched_out,
         "speedup_interleaved_over_wave": None if speedup is None else round(speedup, 4),
+        "planner": {
+            "recommended": rec_cfg,
+            "predicted_units": {"expert_wave": round(pred["candidates"][0]["makespan"], 1),
+                                "interleaved": round(pred["given"]["makespan"], 1),
+                                "recommended": round(rec["makespan"], 1),
+                                "lower_bound": round(pred["lower_bound"], 1)},
+            "predicted_wave_over_interleaved": round(pred["candidates"][0]["makespan"]
+                                                     / max(pred["given"]["makespan"], 1e-9), 4),
+            "measured_wave_over_interleaved": None if speedup is None else round(speedup, 4),
+            "measured_recommended_over_interleaved": round(
+                statistics.median(per["recommended"]) / statistics.median(per["interleaved"]), 4)
+            if per["recommended"] and per["interleaved"] else None,
+        },
         "roofline": roof,
         "cpu_baseline": cpu,
         "input_gen_s": round(t_gen, 1),

@@ -236,6 +236,62 @@ int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,
                           void* const* combine_slices, float* y_local,
                           int32_t* report, void* stream);
 
+/* One schedule configuration and what the planner's model predicts for it. */
+typedef struct {
+  int32_t schedule;          /* moe_schedule                                             */
+  int32_t lead_d;            /* Interleaved lead D (0 for Expert-Wave)                   */
+  int32_t experts_per_wave;  /* Expert-Wave wave size (0 = the automatic wave rule)      */
+  double makespan;           /* predicted kernel time in model units (see below)         */
+  double working_set;        /* time-averaged bytes of the expert weight matrices (an
+                                expert's W1 or W2) that running tasks read              */
+} moe_schedule_estimate;
+
+#define MOE_MAX_SCHEDULE_CANDIDATES 8
+
+typedef struct {
+  moe_schedule_estimate given;        /* the configuration passed in `params`            */
+  moe_schedule_estimate recommended;  /* the planner's choice among the candidates       */
+  moe_schedule_estimate candidates[MOE_MAX_SCHEDULE_CANDIDATES];
+  int32_t num_candidates;
+  int32_t sched_rows;                 /* P for these counts                              */
+  double lower_bound;                 /* total task cost / G, in model units             */
+} moe_schedule_prediction;
+
+/* Schedule planner for one routing (the X-Stage paper, section 6.3,
+ * "Adaptive Burst Shaping and Scope": weigh each order's predicted stall
+ * against its weight locality for the current routing and working set and
+ * pick the original or the interleaved order; section 4.2 on the lead D:
+ * below the knee of Eq. 16 Linear-2 tiles catch up with Linear-1 and wait,
+ * far above it the concurrent expert-weight working set grows).
+ * Host only; touches no device and enqueues nothing.
+ *
+ * Model: G persistent instances walk exactly the task streams
+ * moe_ffn_forward runs (the kernel's own stream code, built for the host).
+ * A Linear-1 task costs H/128 + 2 units, a Linear-2 task I/128 + 2 (one unit
+ * is one 128-wide K block of the mainloop; 2 stands for the epilogue). A
+ * Linear-2 task of scheduler row p starts once all N1 Linear-1 tasks of p
+ * have ended. An event simulation gives each configuration's makespan and
+ * the time average of the weight bytes in use.
+ *   counts  HOST int32 [L]: routed rows of each local expert (the layout's
+ *           counts, copied to the host by the caller).
+ *   plan    from moe_ffn_plan for the same shape: block_m, n1_tiles,
+ *           n2_tiles, grid and lead_d (the knee) are read.
+ *   params  HOST; the configuration reported as `given` (schedule, lead_d
+ *           with 0 = plan->lead_d, experts_per_wave); NULL = Interleaved at
+ *           plan->lead_d.
+ * Candidates, in this order: Expert-Wave with the automatic wave rule,
+ * Interleaved with D = knee, Expert-Wave with all local experts in one wave,
+ * Interleaved with D = knee/2, 2 knee, 4 knee and P (duplicates dropped).
+ * Recommendation, among the candidates predicted within 2% of the fastest:
+ * the first of the two first candidates (the original order, then the knee
+ * lead), else the one with the smallest working set (the earlier one on a
+ * tie).
+ * Returns MOE_ERR_INVALID_ARG for a NULL pointer, a negative count, counts
+ * whose M-blocks exceed plan->max_sched_rows or plan fields that are not
+ * positive. */
+int32_t moe_predict_schedule(const moe_shape* shape, const moe_plan* plan, const int32_t* counts,
+                             const moe_sched_params* params, moe_schedule_prediction* out);
+
 /* Parameters of the store burst-gap probe. */
 typedef struct {
   int32_t producers;        /* K: concurrent producer workgroups, 1..65535            */

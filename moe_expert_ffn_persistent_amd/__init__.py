@@ -16,10 +16,24 @@ from . import _lib
 from ._lib import (MOE_BF16, MOE_FP8_E4M3, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, MOE_W4A8,
                    MoeError, MoeLayout, MoePlan, MoeSchedParams, MoeShape)
 
-__all__ = ["MoeExpertFFN", "LayoutBuffers", "MoeError", "SCHEDULES", "make_shape",
+__all__ = ["MoeExpertFFN", "LayoutBuffers", "MoeError", "SCHEDULES", "make_shape", "prediction_dict",
            "make_params", "library"]
 
 SCHEDULES = {"expert_wave": MOE_SCHED_EXPERT_WAVE, "interleaved": MOE_SCHED_INTERLEAVED}
+SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
+
+
+def _estimate(e) -> dict:
+    return {"schedule": SCHEDULE_NAMES[e.schedule], "lead_d": e.lead_d,
+            "experts_per_wave": e.experts_per_wave, "makespan": e.makespan,
+            "working_set": e.working_set}
+
+
+def prediction_dict(pred) -> dict:
+    """A moe_schedule_prediction as plain Python values."""
+    return {"given": _estimate(pred.given), "recommended": _estimate(pred.recommended),
+            "candidates": [_estimate(pred.candidates[i]) for i in range(pred.num_candidates)],
+            "sched_rows": pred.sched_rows, "lower_bound": pred.lower_bound}
 DTYPES = {"bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "w4a8": MOE_W4A8}
 
 
@@ -110,6 +124,8 @@ class MoeExpertFFN:
         kw = dict(self.defaults)
         kw.update(over)
         kw.setdefault("status", self.status)
+        if kw["schedule"] == "auto":   # resolved per call by predict_schedule
+            kw["schedule"] = "interleaved"
         return make_params(**kw)
 
     def resolved_plan(self, **over) -> MoePlan:
@@ -126,6 +142,18 @@ class MoeExpertFFN:
                              None if bias is None else bias.data_ptr(), lb.c_struct(),
                              _stream(stream))
         return lb
+
+    def predict_schedule(self, counts=None, **sched) -> dict:
+        """The library's schedule planner (moe_predict_schedule) for the
+        current routing: predicted makespan and weight working set of the
+        configuration in ``sched`` and of each candidate order, and the
+        recommended one. ``counts`` (rows per local expert) defaults to the
+        layout's, copied to the host, which waits for the layout."""
+        if counts is None:
+            counts = self.layout_bufs.counts.cpu().tolist()
+        knee_plan = self.resolved_plan(**dict(sched, lead_d=0))
+        return prediction_dict(_lib.predict_schedule(self.shape, knee_plan, counts,
+                                                     self.params(**sched)))
 
     def _check_buffers(self, x_slices, w1, w2, combine_slices, x_scales, w1_scales, w2_scales):
         """The C ABI takes raw pointers; check sizes here so that a mismatch
@@ -172,9 +200,14 @@ class MoeExpertFFN:
                 w2_scales=None, stream=None, **sched):
         """Run Linear-1 + SwiGLU and Linear-2 + weighted combine stores for
         every local expert, in the schedule given by ``sched`` (defaults from
-        the constructor)."""
+        the constructor). ``schedule="auto"`` runs the planner's recommendation
+        for the current routing (predict_schedule; it waits for the layout)."""
         if self.num_tokens:
             self._check_buffers(x_slices, w1, w2, combine_slices, x_scales, w1_scales, w2_scales)
+        if sched.get("schedule", self.defaults["schedule"]) == "auto":
+            rec = self.predict_schedule(**{k: v for k, v in sched.items() if k != "schedule"})["recommended"]
+            sched = dict(sched, schedule=rec["schedule"], lead_d=rec["lead_d"],
+                         experts_per_wave=rec["experts_per_wave"])
         params = self.params(**sched)
         ptr = lambda t: None if t is None else t.data_ptr()
         _lib.ffn_forward(self.shape, self.layout_bufs.c_struct(),

@@ -26,7 +26,7 @@ MOE_MAX_SLICES = 64
 # every symbol include/moe_ffn.h declares
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_scratch_bytes", "moe_ffn_plan",
            "moe_workspace_init", "moe_dispatch_layout", "moe_ffn_forward", "moe_combine_check",
-           "moe_store_burst_probe")
+           "moe_store_burst_probe", "moe_predict_schedule")
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -57,6 +57,18 @@ class MoePlan(ctypes.Structure):
                 ("wall_clock_khz", c_i32)]
 
 TRACE_WORDS = 10
+MAX_SCHEDULE_CANDIDATES = 8
+
+
+class MoeScheduleEstimate(ctypes.Structure):
+    _fields_ = [("schedule", c_i32), ("lead_d", c_i32), ("experts_per_wave", c_i32),
+                ("makespan", ctypes.c_double), ("working_set", ctypes.c_double)]
+
+
+class MoeSchedulePrediction(ctypes.Structure):
+    _fields_ = [("given", MoeScheduleEstimate), ("recommended", MoeScheduleEstimate),
+                ("candidates", MoeScheduleEstimate * MAX_SCHEDULE_CANDIDATES),
+                ("num_candidates", c_i32), ("sched_rows", c_i32), ("lower_bound", ctypes.c_double)]
 
 
 class MoeBurstParams(ctypes.Structure):
@@ -105,6 +117,9 @@ def load(path: str | None = None):
     lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp]
     lib.moe_store_burst_probe.restype = c_i32
     lib.moe_store_burst_probe.argtypes = [P(MoeBurstParams), c_vp, ctypes.c_size_t, c_vp, c_vp]
+    lib.moe_predict_schedule.restype = c_i32
+    lib.moe_predict_schedule.argtypes = [P(MoeShape), P(MoePlan), P(c_i32), P(MoeSchedParams),
+                                         P(MoeSchedulePrediction)]
     _lib = lib
     return lib
 
@@ -167,3 +182,13 @@ def store_burst_probe(params: MoeBurstParams, dst_ptr: int, dst_bytes: int, stam
                       stream: int):
     check(load().moe_store_burst_probe(ctypes.byref(params), dst_ptr, dst_bytes, stamps_ptr, stream),
           "moe_store_burst_probe")
+
+
+def predict_schedule(shape: MoeShape, plan: MoePlan, counts, params: MoeSchedParams | None):
+    """counts: host sequence of L ints (rows of each local expert)."""
+    arr = (c_i32 * max(1, len(counts)))(*[int(c) for c in counts])
+    out = MoeSchedulePrediction()
+    check(load().moe_predict_schedule(ctypes.byref(shape), ctypes.byref(plan), arr,
+                                      None if params is None else ctypes.byref(params),
+                                      ctypes.byref(out)), "moe_predict_schedule")
+    return out

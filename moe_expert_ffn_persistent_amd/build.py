@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmoe_ffn.so")
 ARCH = "gfx950"
 
 SOURCES = ["layout.hip", "ffn_bf16.hip", "ffn_fp8.hip", "ffn_w4a8.hip", "combine.hip", "burst.hip",
-           "api.cpp"]
+           "api.cpp", "planner.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

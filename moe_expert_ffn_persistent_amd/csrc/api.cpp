@@ -136,6 +136,9 @@ WsLayout carve(const moe_shape* s, int block_m, int max_rows) {
 }
 
 }  // namespace
+
+bool shape_valid(const moe_shape* s) { return shape_ok(s); }
+
 }  // namespace moe
 
 using namespace moe;

@@ -103,4 +103,7 @@ hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
+// The shape checks every entry point makes (api.cpp).
+bool shape_valid(const moe_shape* s);
+
 }  // namespace moe

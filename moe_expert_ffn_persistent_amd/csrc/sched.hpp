@@ -31,14 +31,22 @@ struct Task {
   int n;      // N-tile
 };
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// The streams below also run on the host, in the schedule planner's model of
+// the kernel (planner.cpp), so that the model walks exactly these streams.
+__host__ __device__ __forceinline__ int uni(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(v);
+#else
+  return v;
+#endif
+}
 
 struct InterleavedStream {
   int k1, k2, G, P, N1, N2, D;
-  __device__ void init(int g, int G_, int P_, int N1_, int N2_, int D_) {
+  __host__ __device__ void init(int g, int G_, int P_, int N1_, int N2_, int D_) {
     k1 = g; k2 = g; G = G_; P = P_; N1 = N1_; N2 = N2_; D = D_;
   }
-  __device__ Task next() {
+  __host__ __device__ Task next() {
     const int t1 = P * N1, t2 = P * N2;
     if (k1 >= t1 && k2 >= t2) return Task{0, 0, 0};
     const int p1 = k1 < t1 ? k1 / N1 : 0x7fffffff;
@@ -60,12 +68,12 @@ struct ExpertWaveStream {
   int g, G, N1, N2, w, phase, c, nwaves;
   const int* tile_off;        // LDS
   const uint16_t* wave_exp;   // LDS
-  __device__ void init(int g_, int G_, int N1_, int N2_, const int* tile_off_, const uint16_t* wave_exp_,
-                       int nwaves_) {
+  __host__ __device__ void init(int g_, int G_, int N1_, int N2_, const int* tile_off_,
+                                const uint16_t* wave_exp_, int nwaves_) {
     g = g_; G = G_; N1 = N1_; N2 = N2_; tile_off = tile_off_; wave_exp = wave_exp_; nwaves = nwaves_;
     w = 0; phase = 0; c = g_;
   }
-  __device__ Task next() {
+  __host__ __device__ Task next() {
     while (w < nwaves) {
       const int r0 = uni(tile_off[wave_exp[w]]);
       const int rows = uni(tile_off[wave_exp[w + 1]]) - r0;
@@ -96,7 +104,7 @@ struct ExpertWaveStream {
 // Greedy wave grouping over local experts, written to LDS by one thread.
 // Returns the number of waves; wave_exp gets nwaves + 1 boundaries (expert
 // indices, at most L <= MOE_MAX_LOCAL_EXPERTS).
-__device__ inline int build_waves(const int* tile_off, int L, int N1, int G, int experts_per_wave,
+__host__ __device__ inline int build_waves(const int* tile_off, int L, int N1, int G, int experts_per_wave,
                                   uint16_t* wave_exp) {
   int nw = 0;
   int start = tile_off[0];

@@ -273,6 +273,34 @@ def test_all_tokens_on_one_expert_many_blocks():
             _check_against_oracle(up, ref)
 
 
+def test_auto_schedule_runs_the_planners_choice():
+    # many-block experts, so the candidate orders differ; the planner reads
+    # the layout's counts (copied to the host) and forward(schedule="auto")
+    # runs its recommendation, which must match the oracle and be bitwise
+    # identical to both explicit orders (orders never change outputs)
+    wl = _small_wl(tokens_per_slice=400, num_slices=4, num_local=6, num_experts=12, top_k=2,
+                   hidden=512, inter=256, seed=4242)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl, tile=3, grid=96)
+    _route_and_layout(ffn, up)
+    pred = ffn.predict_schedule()
+    print(f"[ffn] planner P={pred['sched_rows']} recommended={pred['recommended']}", flush=True)
+    assert pred["sched_rows"] == int(ffn.layout_bufs.totals[1].item())
+    assert pred["recommended"] in pred["candidates"]
+    bits = {}
+    for sched in ("auto", "expert_wave", "interleaved"):
+        up.reset_combine()
+        run_forward(ffn, up, schedule=sched)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        bits[sched] = up.combine_bits().copy()
+        if sched == "auto":
+            _check_against_oracle(up, ref)
+    assert (bits["auto"] == bits["expert_wave"]).all() and (bits["auto"] == bits["interleaved"]).all()
+
+
 @pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_h_handoff_across_calls_with_poisoned_workspace(tile):
     # h crosses XCDs inside one launch; poisoning the h region between calls
