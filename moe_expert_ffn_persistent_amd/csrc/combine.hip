@@ -8,8 +8,11 @@
 // caller filled them with: every local slot must have been written, and no
 // other slot may have been touched.
 //
-// One workgroup per token; each thread owns 8 consecutive hidden elements
-// (one 16-byte load per slot), so the reads of a slot are fully coalesced.
+// One workgroup per token; each thread owns chunks of 8 consecutive hidden
+// elements (one 16-byte load per slot, so the reads of a slot are fully
+// coalesced), up to kChunks of them at a time: a slot's loads of all of a
+// thread's chunks are issued together, ahead of the arithmetic and of the
+// y_local stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -18,6 +21,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kChunks = 4;   // chunks per thread in flight (H <= 8192 in one pass)
 
 __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
   __shared__ int s_cnt[4];   // unwritten, clobbered, nonfinite flags; [3]: local-slot mask
@@ -32,34 +36,55 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
   __syncthreads();
   const int local_mask = s_cnt[3];
   int unwritten = 0, clobbered = 0, nonfinite = 0;
-  const char* base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
-  for (int c = threadIdx.x; c < a.H / 8; c += kThreads) {
-    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const char* __restrict__ base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
+  float* __restrict__ yrow = a.y ? a.y + (size_t)n * a.H : nullptr;
+  const int nchunk = a.H / 8;
+  for (int c0 = 0; c0 < nchunk; c0 += kChunks * kThreads) {
+    float y[kChunks][8];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[u][i] = 0.f;
     for (int j = 0; j < a.k; ++j) {
       const bool local = (local_mask >> j) & 1;
       if (!local && !audit) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + ((size_t)j * a.H + c * 8) * 2);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint4 v[kChunks];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const float f = __uint_as_float(bits << 16);
-        if (local) {
-          y[i] += f;
-          if (audit) {
-            if (bits == 0xFFFFu) unwritten |= 1 << j;
-            else if (!isfinite(f)) nonfinite |= 1 << j;
+      for (int u = 0; u < kChunks; ++u) {
+        const int c = c0 + u * kThreads + (int)threadIdx.x;
+        if (c < nchunk) v[u] = *reinterpret_cast<const uint4*>(base + ((size_t)j * a.H + c * 8) * 2);
+      }
+#pragma unroll
+      for (int u = 0; u < kChunks; ++u) {
+        const int c = c0 + u * kThreads + (int)threadIdx.x;
+        if (c >= nchunk) continue;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+          const float f = __uint_as_float(bits << 16);
+          if (local) {
+            y[u][i] += f;
+            if (audit) {
+              if (bits == 0xFFFFu) unwritten |= 1 << j;
+              else if (!isfinite(f)) nonfinite |= 1 << j;
+            }
+          } else if (bits != 0xFFFFu) {
+            clobbered |= 1 << j;
           }
-        } else if (bits != 0xFFFFu) {
-          clobbered |= 1 << j;
         }
       }
     }
-    if (a.y) {   // streamed out: not re-read here
+    if (yrow) {   // streamed out: not re-read here
       typedef float f32x4 __attribute__((ext_vector_type(4)));
-      f32x4* dst = reinterpret_cast<f32x4*>(a.y + (size_t)n * a.H + c * 8);
-      __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, dst);
-      __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, dst + 1);
+#pragma unroll
+      for (int u = 0; u < kChunks; ++u) {
+        const int c = c0 + u * kThreads + (int)threadIdx.x;
+        if (c >= nchunk) continue;
+        f32x4* dst = reinterpret_cast<f32x4*>(yrow + c * 8);
+        __builtin_nontemporal_store(f32x4{y[u][0], y[u][1], y[u][2], y[u][3]}, dst);
+        __builtin_nontemporal_store(f32x4{y[u][4], y[u][5], y[u][6], y[u][7]}, dst + 1);
+      }
     }
   }
   if (audit) {
