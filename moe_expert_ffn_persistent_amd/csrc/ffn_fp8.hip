@@ -13,10 +13,10 @@
 //    the whole K block, and each block is promoted right behind the matrix
 //    core, which keeps the register budget of a 192 x 256 tile within eight
 //    wavefronts (fewer copy bytes per FLOP than 128 x 256).
-//  - Weight rows and token rows sit in two LDS rings. The default tile gives
-//    the weights one stage more than the tokens (three against two, which
-//    is what 160 KiB holds at 192 x 256): a weight stage is copied two
-//    stages ahead, a token stage one stage ahead.
+//  - Weight rows and token rows sit in two LDS rings, and one of them may be
+//    a stage deeper (three stages against two is what 160 KiB holds at
+//    192 x 256). The default tile gives the tokens the third stage: a token
+//    stage is copied two stages ahead of use, a weight stage one.
 //  - Token scales of the stage are copied into LDS next to the token rows
 //    by four-byte direct-to-LDS copies; the weight scales of the task (two
 //    128-row blocks) are staged in LDS once per task.
@@ -39,10 +39,12 @@ template <int TM_, int TN_, int WT_, int WF_, int NS_, bool WIDE_ = false, int S
           int XW_ = 0>
 struct Cfg8 {
   static constexpr int TM = TM_, TN = TN_, WT = WT_, WF = WF_, NS = NS_;
-  // ring depths: NS token stages and NS + XW weight stages (XW = 1: a
-  // weight stage is copied two stages ahead, a token stage one stage ahead)
-  static constexpr int XW = XW_, NST = NS, NSW = NS + XW;
-  static_assert(XW == 0 || XW == 1, "weight ring at most one stage deeper");
+  // ring depths: XW = 1 gives the weights one stage more than the tokens
+  // (a weight stage is copied two stages ahead of use, a token stage one),
+  // XW = -1 the tokens one stage more than the weights
+  static constexpr int XW = XW_;
+  static constexpr int NSW = NS + (XW > 0 ? 1 : 0), NST = NS + (XW < 0 ? 1 : 0);
+  static_assert(XW >= -1 && XW <= 1, "one ring at most one stage deeper");
   // WIDE: 16x16x128 MFMAs (one per output block and K block), promoted
   // block by block between them (Tile8W); else 32x32x64 MFMAs (Tile8)
   static constexpr bool WIDE = WIDE_;
@@ -66,12 +68,12 @@ struct Cfg8 {
   static constexpr int LDS_BYTES = T_RING + NST * T_BYTES;
   static constexpr uint32_t w_off(int s) { return s * W_BYTES; }
   static constexpr uint32_t t_off(int s) { return T_RING + s * T_BYTES; }
-  // copy issued o-th in a stage: with a deeper weight ring the token copies
-  // (awaited one stage later) go first, since copies complete in issue order
-  static constexpr int copy_of(int o) { return XW == 0 ? o : (o < NTC ? NIW + o : o - NTC); }
-  // copies still in flight when a stage's operands have landed: the weights
-  // of the stage after next (XW = 1), the stages after next (NS > 2)
-  static constexpr int WAIT = (XW ? NIW : 0) + NI * (NST - 2);
+  // copy issued o-th in a stage: the copies of the shallower ring (awaited
+  // one stage later) go first, since copies complete in issue order
+  static constexpr int copy_of(int o) { return XW <= 0 ? o : (o < NTC ? NIW + o : o - NTC); }
+  // copies still in flight when a stage's operands have landed: those of
+  // the deeper ring for the stage after next, and whole stages (NS > 2)
+  static constexpr int WAIT = (XW > 0 ? NIW : XW < 0 ? NTC : 0) + NI * (NS - 2);
   // MFMAs per wavefront per stage: one 16x16x128 per 16 x 16 block (WIDE), or
   // two 32x32x64 per 32 x 32 block
   static constexpr int NM = WIDE ? (FT / 16) * (TT / 16) : 2 * FB * TB;
@@ -87,7 +89,7 @@ struct Cfg8 {
   static_assert(TT % 32 == 0 && FT % 32 == 0 && FB % 2 == 0, "wavefront tile");
   static_assert(((TN + TM) / RPI) % NW == 0, "copies split evenly");
   static_assert(TN % (RPI * NW) == 0, "every wavefront copies weight rows in its first NIW instructions");
-  static_assert(NS >= 2 && NI * NSW <= 63, "vmcnt range");
+  static_assert(NS >= 2 && NI * (NS + 1) <= 63, "vmcnt range");
   static_assert(W_BYTES % 1024 == 0 && T_BYTES % 1024 == 0, "1 KiB copy slots");
 };
 
@@ -174,7 +176,7 @@ struct Tile8Copies {
                                         bool l1) {
     lds_barrier();
 #pragma unroll
-    for (int v = 1 - C::NSW; v < 0; ++v) {
+    for (int v = 1 - (C::NSW > C::NST ? C::NSW : C::NST); v < 0; ++v) {
       const int st = v + C::NST - 1, sw_ = v + C::NSW - 1;
 #pragma unroll
       for (int o = 0; o < C::NI; ++o) {
@@ -770,6 +772,9 @@ using Cfg8Wide3 = Cfg8<128, 256, 2, 4, 3, true>;  // 64 x 64 per wavefront, 16x1
 // (a weight stage is copied two stages ahead), copies spread over the whole
 // stage
 using Cfg8WideS = Cfg8<192, 256, 2, 4, 2, true, 8, 1>;
+// as Cfg8WideS with the tokens in the deeper ring (gathered token rows come
+// back later than the weights' consecutive rows), copies over six eighths
+using Cfg8WideT = Cfg8<192, 256, 2, 4, 2, true, 6, -1>;
 
 template <class C>
 hipError_t launch(const FfnArgs& a, hipStream_t s) {
@@ -787,7 +792,8 @@ hipError_t occupancy(int* n) {
 extern const TileInfo kFp8Tiles[];
 extern const int kNumFp8Tiles;
 const TileInfo kFp8Tiles[] = {
-    {25, MOE_FP8_E4M3, Cfg8WideS::TM, Cfg8WideS::TN, Cfg8WideS::THREADS},   // first fitting tile is the default
+    {26, MOE_FP8_E4M3, Cfg8WideT::TM, Cfg8WideT::TN, Cfg8WideT::THREADS},   // first fitting tile is the default
+    {25, MOE_FP8_E4M3, Cfg8WideS::TM, Cfg8WideS::TN, Cfg8WideS::THREADS},
     {23, MOE_FP8_E4M3, Cfg8Wide::TM, Cfg8Wide::TN, Cfg8Wide::THREADS},
     {22, MOE_FP8_E4M3, Cfg8W8::TM, Cfg8W8::TN, Cfg8W8::THREADS},
     {24, MOE_FP8_E4M3, Cfg8Wide3::TM, Cfg8Wide3::TN, Cfg8Wide3::THREADS},
@@ -802,6 +808,7 @@ hipError_t launch_ffn_fp8(int id, const FfnArgs& a, hipStream_t s) {
     case 23: return launch<Cfg8Wide>(a, s);
     case 24: return launch<Cfg8Wide3>(a, s);
     case 25: return launch<Cfg8WideS>(a, s);
+    case 26: return launch<Cfg8WideT>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -813,6 +820,7 @@ hipError_t occupancy_ffn_fp8(int id, int* n) {
     case 23: return occupancy<Cfg8Wide>(n);
     case 24: return occupancy<Cfg8Wide3>(n);
     case 25: return occupancy<Cfg8WideS>(n);
+    case 26: return occupancy<Cfg8WideT>(n);
   }
   return hipErrorInvalidValue;
 }

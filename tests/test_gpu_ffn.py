@@ -335,7 +335,7 @@ TOL_FP8 = 5e-2
 TOL_W4A8 = 8e-2
 
 
-FP8_TILES = [21, 22, 23, 24, 25]
+FP8_TILES = [21, 22, 23, 24, 25, 26]
 
 
 @pytest.mark.parametrize("tile", FP8_TILES)
