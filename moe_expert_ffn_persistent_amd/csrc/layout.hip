@@ -10,7 +10,8 @@
 //
 // Kernels, all launched on the caller's stream, no host round trip:
 //   route_topk    one wavefront per token: k rounds of a wavefront argmax
-//                 over (z desc, index asc), softmax over the kept z.
+//                 over (z desc, index asc) by DPP reductions of order keys,
+//                 softmax over the kept z.
 //   layout_count  one wavefront per chunk of 256 flat pairs: per-expert
 //                 counts of the chunk.
 //   layout_scan   one workgroup: wavefront prefix scans over the chunk
@@ -21,6 +22,8 @@
 //                 grouped with ballots and ranked by the popcount of the
 //                 lower lanes, so rows of an expert keep ascending f.
 #include <hip/hip_runtime.h>
+
+#include <climits>
 
 #include "internal.hpp"
 
@@ -56,17 +59,50 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// PER: logits per lane (E <= 64 * PER); instantiated for PER = 1, 2, 4, 8, 16
+// Order-preserving integer key of a float: keys compare like the values,
+// -0 and +0 get the same key, and NaN gets a key below every number (a
+// stable descending sort puts it last).
+__device__ __forceinline__ int order_key(float z) {
+  if (z != z) return INT_MIN + 1;
+  if (z == 0.f) return 0;
+  const int b = __float_as_int(z);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+
+// Wavefront maximum (kMin) or minimum of v, returned to every lane. Lane 15
+// of each row gathers its row with four row shifts, row broadcasts carry
+// rows 0 and 2 into rows 1 and 3 and then row 1 into rows 2 and 3, so lane 63
+// ends up holding the result. Lanes whose shifted source lies outside the
+// row keep the identity.
+template <bool kMin>
+__device__ __forceinline__ int wave_extreme(int v) {
+  constexpr int id = kMin ? INT_MAX : INT_MIN;
+  auto f = [](int a, int b) { return kMin ? min(a, b) : max(a, b); };
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// PER: logits per lane (E <= 64 * PER); instantiated for PER = 1, 2, 4, 8, 16.
+// Lane l holds experts l, l+64, ... Each of the k rounds takes every lane's
+// best remaining expert (largest key, then lowest index, which within a lane
+// is the lowest slot), the wavefront's largest key, and, among the lanes
+// holding it, the lowest expert index (a second reduction only when several
+// lanes tie); the winning lane retires that expert.
 template <int PER>
 __global__ void __launch_bounds__(256) route_topk(LayoutArgs a) {
-  constexpr int kMaxPerLane = PER;
   const int lane = threadIdx.x & (kWave - 1);
   const int n = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (n >= a.N) return;
-  float z[kMaxPerLane];
+  float z[PER];
+  int key[PER];
   const float* row = a.logits + (size_t)n * a.E;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = lane + i * kWave;
     float v = -INFINITY;
     if (e < a.E) {
@@ -74,34 +110,41 @@ __global__ void __launch_bounds__(256) route_topk(LayoutArgs a) {
       if (a.bias) v = v + a.bias[e];
     }
     z[i] = v;
+    key[i] = e < a.E ? order_key(v) : INT_MIN;   // below NaN: never taken while k <= E
   }
-  unsigned taken = 0;   // bit i: element i of this lane already selected
-  float myz = 0.f;      // lane j < k keeps the j-th selection
+  float myz = 0.f;   // lane j < k keeps the j-th selection
   int myi = 0;
   for (int j = 0; j < a.k; ++j) {
-    float bz = -INFINITY;
-    int bi = 0x7fffffff;
+    int hk = key[0], hs = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + i * kWave;
-      if (e < a.E && !(taken & (1u << i)) && better(z[i], e, bz, bi)) {
-        bz = z[i];
-        bi = e;
+    for (int i = 1; i < PER; ++i)
+      if (key[i] > hk) {
+        hk = key[i];
+        hs = i;
       }
+    const int best = wave_extreme<false>(hk);
+    const unsigned long long tied = __ballot(hk == best);
+    int e;
+    if ((tied & (tied - 1)) == 0) {
+      const int wl = __ffsll((long long)tied) - 1;
+      e = wl + kWave * __builtin_amdgcn_readlane(hs, wl);
+    } else {
+      e = wave_extreme<true>(hk == best ? lane + kWave * hs : INT_MAX);
     }
+    const int wl = e & (kWave - 1), ws = e / kWave;
+    float wz = 0.f;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float oz = __shfl_xor(bz, d, kWave);
-      const int oi = __shfl_xor(bi, d, kWave);
-      if (better(oz, oi, bz, bi)) {
-        bz = oz;
-        bi = oi;
-      }
+    for (int i = 0; i < PER; ++i)
+      if (i == ws) wz = z[i];
+    wz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wz), wl));
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == ws) key[i] = INT_MIN;
     }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == j) {
-      myz = bz;
-      myi = bi;
+      myz = wz;
+      myi = e;
     }
   }
   // softmax over the kept values; the first selection is the largest

@@ -80,6 +80,34 @@ def test_layout_from_given_topk_and_ties():
     _check_layout(wl, lb, idx2, w2, ffn.plan.block_m, routed=False)
 
 
+def test_routing_ties_across_lanes_and_slots():
+    # 256 experts: lane l of the routing wavefront holds experts l, l+64, l+128
+    # and l+192, so equal logits can tie within a lane (different slots) and
+    # across lanes; -0 and +0 must tie; NaN sorts after every number and
+    # -inf after every finite value (a stable sort of -z)
+    wl = mi.Workload("ties256", 2, 32, 256, 8, 0, 32, 256, 128, "bf16", False, 7)
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((64, 256)).astype(np.float32)
+    logits[:16] = 0.0
+    logits[:16][rng.random((16, 256)) < 0.5] = -0.0          # mixed-sign zeros: experts 0..7 win
+    logits[16:32] = -np.abs(logits[16:32]) - 1.0
+    logits[16:32][:, [200, 136, 72, 8, 64, 128, 192, 0]] = 1.0
+    for r in range(32, 48):
+        cols = rng.choice(256, 12, replace=False)
+        logits[r, cols[:6]] = np.nan
+        logits[r, cols[6:]] = -np.inf
+    logits[48:56, :250] = -np.inf                             # the finite six, then -inf by index
+    idx_ref, w_ref = mo.route(logits, None, 8)
+    assert (idx_ref[:16] == np.arange(8)).all()
+    assert (idx_ref[16:32] == [0, 8, 64, 72, 128, 136, 192, 200]).all()
+    assert (np.sort(idx_ref[48:56, :6], axis=1) == np.arange(250, 256)).all()
+    assert (idx_ref[48:56, 6:] == [0, 1]).all()
+    ffn = make_ffn(wl)
+    lb = ffn.layout(logits=to_dev(logits))
+    torch.cuda.synchronize()
+    _check_layout(wl, lb, idx_ref, w_ref, ffn.plan.block_m)
+
+
 def test_layout_empty_batch():
     wl = mi.Workload("empty", 2, 0, 8, 2, 0, 4, 256, 128, "bf16", False, 1)
     ffn = make_ffn(wl)
