@@ -202,6 +202,15 @@ def main():
     # with their default parameters, and the planner's recommendation ----
     arms = {"expert_wave": {"schedule": "expert_wave"}, "interleaved": {"schedule": "interleaved"},
             "recommended": rec_cfg}
+    # the recommendation is timed as an arm of its own only when it is not
+    # one of the two default configurations
+    same_as = None
+    if rec_cfg["schedule"] == "interleaved" and rec_cfg["lead_d"] == ffn.plan.lead_d:
+        same_as = "interleaved"
+    elif rec_cfg["schedule"] == "expert_wave" and rec_cfg["experts_per_wave"] == 0:
+        same_as = "expert_wave"
+    if same_as:
+        del arms["recommended"]
     per = {a: [] for a in arms}
     order = list(arms)
     for r in range(args.pairs):
@@ -297,9 +306,9 @@ def main():
             "predicted_wave_over_interleaved": round(pred["candidates"][0]["makespan"]
                                                      / max(pred["given"]["makespan"], 1e-9), 4),
             "measured_wave_over_interleaved": None if speedup is None else round(speedup, 4),
+            "recommended_is": same_as,
             "measured_recommended_over_interleaved": round(
-                statistics.median(per["recommended"]) / statistics.median(per["interleaved"]), 4)
-            if per["recommended"] and per["interleaved"] else None,
+                statistics.median(per[same_as or "recommended"]) / statistics.median(per["interleaved"]), 4),
         },
         "roofline": roof,
         "cpu_baseline": cpu,
