@@ -281,7 +281,8 @@ typedef struct {
  *           plan->lead_d.
  * Candidates, in this order: Expert-Wave with the automatic wave rule,
  * Interleaved with D = knee, Expert-Wave with all local experts in one wave,
- * Interleaved with D = knee/2, 2 knee, 4 knee and P (duplicates dropped).
+ * Interleaved with D = knee/2, 2 knee, 4 knee and P, each capped at P (a
+ * lead of P or more behaves as P; duplicates dropped).
  * Recommendation, among the candidates predicted within 2% of the fastest:
  * the first of the two first candidates (the original order, then the knee
  * lead), else the one with the smallest working set (the earlier one on a

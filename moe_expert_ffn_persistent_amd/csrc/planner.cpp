@@ -194,7 +194,12 @@ extern "C" int32_t moe_predict_schedule(const moe_shape* s, const moe_plan* plan
   r.candidates[n++] = config(MOE_SCHED_EXPERT_WAVE, 0, 0);
   r.candidates[n++] = config(MOE_SCHED_INTERLEAVED, knee, 0);
   if (m.L > 1) r.candidates[n++] = config(MOE_SCHED_EXPERT_WAVE, 0, m.L);
-  const int leads[4] = {std::max(1, knee / 2), 2 * knee, 4 * knee, std::max(1, m.P)};
+  // a lead of P or more behaves as P (Linear-2 waits until every Linear-1
+  // tile is out), so candidate leads are capped at P
+  const long long cap = std::max(1, m.P);
+  const int leads[4] = {(int)std::min<long long>(std::max(1, knee / 2), cap),
+                        (int)std::min<long long>(2ll * knee, cap), (int)std::min<long long>(4ll * knee, cap),
+                        (int)cap};
   for (int i = 0; i < 4; ++i) {
     bool dup = false;
     for (int j = 0; j < n; ++j)

@@ -49,9 +49,13 @@ struct InterleavedStream {
   __host__ __device__ Task next() {
     const int t1 = P * N1, t2 = P * N2;
     if (k1 >= t1 && k2 >= t2) return Task{0, 0, 0};
-    const int p1 = k1 < t1 ? k1 / N1 : 0x7fffffff;
+    // p1 is unbounded once the Linear-1 stream is exhausted: the Linear-2
+    // tile is then taken whatever the lead (a lead near INT_MAX must not
+    // turn the comparison around and hand out a Linear-1 tile past the end)
+    const bool l1_done = k1 >= t1;
+    const int p1 = l1_done ? 0 : k1 / N1;
     const int p2 = k2 / N2;
-    if (k2 < t2 && (long long)p2 + D <= (long long)p1) {
+    if (k2 < t2 && (l1_done || (long long)p2 + D <= (long long)p1)) {
       Task t{2, p2, k2 - p2 * N2};
       k2 += G;
       return t;

@@ -111,7 +111,10 @@ def test_weights_scale_outputs_exactly():
 
 
 @pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
-@pytest.mark.parametrize("grid,lead,epw", [(1, 1, 0), (3, 1, 1), (5, 2, 0), (7, 100, 2)])
+# a lead of 2^31 - 1 behaves as D >= P: once the Linear-1 stream is out,
+# only Linear-2 tiles follow (no comparison may overflow into a Linear-1
+# tile past the end)
+@pytest.mark.parametrize("grid,lead,epw", [(1, 1, 0), (3, 1, 1), (5, 2, 0), (7, 100, 2), (5, 2 ** 31 - 1, 0)])
 def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
     wl = _small_wl(tokens_per_slice=40, num_local=5, num_experts=10, top_k=3, seed=555)
     inp = mi.make_inputs(wl)

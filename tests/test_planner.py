@@ -183,9 +183,15 @@ def test_candidate_list():
     kinds = [(e["schedule"], e["lead_d"], e["experts_per_wave"]) for e in pred["candidates"]]
     P = pred["sched_rows"]
     assert P == 8 + 5 + 4
+    # leads of P or more behave as P and are capped there (2 knee = 20 and
+    # 4 knee = 40 both become P = 17), duplicates dropped
     assert kinds == [("expert_wave", 0, 0), ("interleaved", 10, 0), ("expert_wave", 0, 3),
-                     ("interleaved", 5, 0), ("interleaved", 20, 0), ("interleaved", 40, 0),
-                     ("interleaved", P, 0)]
+                     ("interleaved", 5, 0), ("interleaved", P, 0)]
+    # a huge knee does not overflow: every interleaved candidate is capped at P
+    pred = _predict([500, 300, 200], 64, 4, 6, 40, (1 << 31) - 1, 256, 256)
+    leads = [e["lead_d"] for e in pred["candidates"] if e["schedule"] == "interleaved"]
+    assert leads[0] == (1 << 31) - 1 and all(d == P for d in leads[1:])
+    assert pred["candidates"][1]["makespan"] == pred["candidates"][-1]["makespan"]
 
 
 def test_invalid_arguments():
