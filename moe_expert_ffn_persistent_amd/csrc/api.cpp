@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <climits>
 #include <mutex>
 
 #include "internal.hpp"
@@ -227,6 +228,10 @@ int32_t moe_ffn_plan(const moe_shape* s, const moe_sched_params* prm, moe_plan* 
   const long long pairs = num_tokens(s) * s->top_k;
   long long rows = (pairs + (long long)s->num_local_experts * (t->block_m - 1)) / t->block_m;
   p.max_sched_rows = (int)std::max<long long>(rows, 1);
+  // the task streams count tiles in int: every tile index plus one grid
+  // stride must stay below INT_MAX
+  if (std::max<long long>(rows, 1) * std::max(p.n1_tiles, p.n2_tiles) + grid >= INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
   p.workspace_bytes = carve(s, p.block_m, p.max_sched_rows).total;
   p.wall_clock_khz = dp->wall_khz;
   *out = p;

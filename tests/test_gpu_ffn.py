@@ -469,3 +469,17 @@ def test_wrapper_rejects_mismatched_buffers_before_launch():
         ffn.forward(up.x_slices[:-1], up.w1, up.w2, up.comb_slices)
     torch.cuda.synchronize()
     assert int(ffn.status.item()) == 0
+
+
+def test_plan_rejects_shapes_whose_tile_counts_overflow():
+    # 2^30 routed pairs through the 32-row decode tile at H = 8192: up to 2^25
+    # scheduler rows x 64 Linear-2 N-tiles would overflow the streams' int tile
+    # indices, so the plan is refused (nothing is allocated or launched)
+    from moe_expert_ffn_persistent_amd import make_params, make_shape
+    shape = make_shape(1, 1 << 26, 16, 16, 0, 16, 8192, 1024, "bf16")
+    with pytest.raises(_lib.MoeError) as err:
+        _lib.ffn_plan(shape, make_params(tile=3))
+    assert err.value.status == _lib.MOE_ERR_UNSUPPORTED
+    # the same shape through the 256-row tile fits
+    plan = _lib.ffn_plan(shape, make_params(tile=7))
+    assert plan.max_sched_rows * max(plan.n1_tiles, plan.n2_tiles) < 2 ** 31 - plan.grid
