@@ -118,6 +118,8 @@ def main():
                          "resolved once before the timed region")
     ap.add_argument("--pairs", type=int, default=10, help="A-B-B-A rounds of the schedule comparison")
     ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--tokens-per-slice", type=int, default=0,
+                    help="run the workload's shapes at another batch size (workload name gets @T<n>)")
     ap.add_argument("--lead-d", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -131,6 +133,8 @@ def main():
         sys.exit(2)
 
     wl = mi.get_workload(args.workload)
+    if args.tokens_per_slice > 0:
+        wl = wl.with_tokens(args.tokens_per_slice)
     t_gen = time.perf_counter()
     inp = mi.make_inputs(wl, workers=min(16, os.cpu_count() or 1))   # before any GPU call
     t_gen = time.perf_counter() - t_gen

@@ -483,3 +483,16 @@ def test_plan_rejects_shapes_whose_tile_counts_overflow():
     # the same shape through the 256-row tile fits
     plan = _lib.ffn_plan(shape, make_params(tile=7))
     assert plan.max_sched_rows * max(plan.n1_tiles, plan.n2_tiles) < 2 ** 31 - plan.grid
+
+
+@pytest.mark.parametrize("name,T,want", [("dsv3", 512, 5), ("dsv3", 1024, 5), ("dsv3", 768, 7), ("dsv3", 2048, 7),
+                                         ("qwen3_prefill", 8192, 7), ("qwen3_decode", 16, 3)])
+def test_automatic_bf16_tile_choice(name, T, want):
+    # the 256-row tile unless experts sit just past a multiple of 256 rows
+    # (expected padded rows > 1.35x those of the 160-row tile with padding
+    # skipped), where the 160-row tile was measured 1.45x faster
+    from moe_expert_ffn_persistent_amd import make_params, make_shape
+    wl = mi.get_workload(name)
+    shape = make_shape(wl.num_slices, T, wl.num_experts, wl.top_k, wl.local_begin, wl.num_local, wl.hidden,
+                       wl.inter, "bf16")
+    assert _lib.ffn_plan(shape, make_params()).tile == want
