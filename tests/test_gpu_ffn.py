@@ -240,6 +240,40 @@ def test_combine_check_reduce_and_audit():
     assert report.cpu().tolist()[:2] == [1, 1]
 
 
+def test_abi_maximum_sizes():
+    # every table at its ABI limit: 64 source slices (MOE_MAX_SLICES), 1024
+    # global experts (16 logits per lane of the routing wavefront), top-16,
+    # 256 local experts (MOE_MAX_LOCAL_EXPERTS: scheduler-row offsets and
+    # wave tables at full length); routing, layout, both schedules and the
+    # reduction against the oracle
+    wl = _small_wl(num_slices=64, tokens_per_slice=3, num_experts=1024, top_k=16, local_begin=512,
+                   num_local=256, hidden=256, inter=128, seed=31337)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    assert ref.written.any()
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    print(f"[ffn] maximum sizes tile={ffn.plan.tile}", flush=True)
+    _route_and_layout(ffn, up)
+    bits = {}
+    for sched in ("expert_wave", "interleaved"):
+        up.reset_combine()
+        run_forward(ffn, up, schedule=sched)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        _check_against_oracle(up, ref)
+        bits[sched] = up.combine_bits().copy()
+    assert (bits["expert_wave"] == bits["interleaved"]).all()
+    y = torch.zeros((wl.num_tokens, wl.hidden), dtype=torch.float32, device=dev())
+    report = torch.zeros(4, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, y=y, report=report)
+    torch.cuda.synchronize()
+    assert report.cpu().tolist() == [0, 0, 0, 0]
+    err = row_rel_err(y.cpu().numpy().astype(np.float64), ref.y_local)
+    has = ref.written.any(axis=1)
+    assert err[has].max() <= TOL_BF16
+
+
 def test_empty_batch_and_single_token():
     wl = _small_wl(tokens_per_slice=0)
     ffn = make_ffn(wl)
