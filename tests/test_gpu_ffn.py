@@ -530,3 +530,41 @@ def test_automatic_bf16_tile_choice(name, T, want):
     shape = make_shape(wl.num_slices, T, wl.num_experts, wl.top_k, wl.local_begin, wl.num_local, wl.hidden,
                        wl.inter, "bf16")
     assert _lib.ffn_plan(shape, make_params()).tile == want
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes_against_oracle(case):
+    # seeded random shapes across the three formats: slice counts, ragged
+    # token counts, expert ranges that start mid-way, top-k from 1 to 8,
+    # both schedules with a random grid and lead; every local slot against
+    # the oracle and the two schedules bitwise identical
+    rng = np.random.default_rng(20000 + case)
+    dtype = ["bf16", "fp8", "w4a8"][case % 3]
+    E = int(rng.integers(4, 65))
+    k = int(rng.integers(1, min(8, E) + 1))
+    L = int(rng.integers(1, min(E, 24) + 1))
+    e0 = int(rng.integers(0, E - L + 1))
+    wl = _small_wl(num_slices=int(rng.integers(1, 9)), tokens_per_slice=int(rng.integers(1, 200)),
+                   num_experts=E, top_k=k, local_begin=e0, num_local=L,
+                   hidden=int(rng.choice([256, 512, 768, 1024])), inter=int(rng.choice([128, 256, 384, 640])),
+                   dtype=dtype, seed=30000 + case)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    grid = int(rng.choice([0, 8, 40, 96]))
+    lead = int(rng.choice([0, 1, 3, 1000]))
+    print(f"[ffn] random case {case}: {dtype} S={wl.num_slices} T={wl.tokens_per_slice} E={E} k={k} e0={e0} "
+          f"L={L} H={wl.hidden} I={wl.inter} tile={ffn.plan.tile} grid={grid} D={lead}", flush=True)
+    _route_and_layout(ffn, up)
+    tol = {"bf16": TOL_BF16, "fp8": TOL_FP8, "w4a8": TOL_W4A8}[dtype]
+    bits = {}
+    for sched in ("expert_wave", "interleaved"):
+        up.reset_combine()
+        run_forward(ffn, up, schedule=sched, grid=grid, lead_d=lead)
+        torch.cuda.synchronize()
+        assert int(ffn.status.item()) == 0
+        if ref.written.any():
+            _check_against_oracle(up, ref, tol=tol)
+        bits[sched] = up.combine_bits().copy()
+    assert (bits["expert_wave"] == bits["interleaved"]).all()
