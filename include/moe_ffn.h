@@ -224,12 +224,12 @@ int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
  *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
  *   y_local        [N, H] fp32 or NULL: y_local[n] = sum over the local
  *                  slots j of token n, in ascending j, of combine[n, j].
- *   report         device int32 [4] or NULL; counts are ADDED to it:
- *                  [0] local slots still holding the sentinel 0xFFFF in
- *                      their first element (never written),
- *                  [1] non-local slots whose first element is not the
+ *   report         device int32 [4] or NULL; slot counts are ADDED to it:
+ *                  [0] local slots with an element still holding the
+ *                      sentinel 0xFFFF (not fully written),
+ *                  [1] non-local slots with an element that is not the
  *                      sentinel (written although not local),
- *                  [2] non-finite values in local slots,
+ *                  [2] local slots holding a non-finite value,
  *                  [3] unused (0).
  *                  The audit reads every slot; pass NULL to skip it. */
 int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,

@@ -8,11 +8,13 @@
 // caller filled them with: every local slot must have been written, and no
 // other slot may have been touched.
 //
-// One workgroup per token; each thread owns chunks of 8 consecutive hidden
-// elements (one 16-byte load per slot, so the reads of a slot are fully
-// coalesced), up to kChunks of them at a time: a slot's loads of all of a
-// thread's chunks are issued together, ahead of the arithmetic and of the
-// y_local stores.
+// One workgroup of eight wavefronts per token. Each wavefront reads the
+// token's k row indices itself and ballots them into the local-slot mask, so
+// no LDS or barrier precedes the data loads. Each thread owns quads of 4
+// consecutive hidden elements (an 8-byte load per slot, a 16-byte store), so
+// one load instruction of a wavefront covers 512 contiguous bytes of a slot
+// row and one store 1 KiB of the y row; a thread's loads of all its quads of
+// one slot are issued together, ahead of the arithmetic and of the stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -20,57 +22,56 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunks = 4;   // chunks per thread in flight (H <= 8192 in one pass)
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kQuads = 4;   // quads per thread in flight (H <= 8192 in one pass)
 
 __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
-  __shared__ int s_cnt[4];   // unwritten, clobbered, nonfinite flags; [3]: local-slot mask
+  __shared__ int s_flag[3];   // unwritten, clobbered, nonfinite slots (bit j)
   const int n = blockIdx.x;
   const int s = n / a.T;
   const int t = n - s * a.T;
+  const int lane = threadIdx.x & 63;
   const bool audit = a.report != nullptr;
-  if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
-  __syncthreads();
-  if (threadIdx.x < a.k && a.pair_row[(size_t)n * a.k + threadIdx.x] >= 0)
-    atomicOr(&s_cnt[3], 1 << threadIdx.x);
-  __syncthreads();
-  const int local_mask = s_cnt[3];
-  int unwritten = 0, clobbered = 0, nonfinite = 0;
+  const int pr = lane < a.k ? a.pair_row[(size_t)n * a.k + lane] : -1;
+  const uint32_t local_mask = (uint32_t)__ballot(lane < a.k && pr >= 0);
+  // slots visited in ascending order: the local ones, or all k when auditing
+  const uint32_t visit = audit ? (uint32_t)((1ull << a.k) - 1ull) : local_mask;
+  uint32_t unwritten = 0, clobbered = 0, nonfinite = 0;
   const char* __restrict__ base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
   float* __restrict__ yrow = a.y ? a.y + (size_t)n * a.H : nullptr;
-  const int nchunk = a.H / 8;
-  for (int c0 = 0; c0 < nchunk; c0 += kChunks * kThreads) {
-    float y[kChunks][8];
+  const int nquad = a.H / 4;
+  for (int q0 = 0; q0 < nquad; q0 += kQuads * kThreads) {
+    float y[kQuads][4];
 #pragma unroll
-    for (int u = 0; u < kChunks; ++u)
+    for (int u = 0; u < kQuads; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[u][i] = 0.f;
-    for (int j = 0; j < a.k; ++j) {
+      for (int i = 0; i < 4; ++i) y[u][i] = 0.f;
+    for (uint32_t m = visit; m; m &= m - 1) {
+      const int j = __builtin_ctz(m);
       const bool local = (local_mask >> j) & 1;
-      if (!local && !audit) continue;
-      uint4 v[kChunks];
+      uint2 v[kQuads];
 #pragma unroll
-      for (int u = 0; u < kChunks; ++u) {
-        const int c = c0 + u * kThreads + (int)threadIdx.x;
-        if (c < nchunk) v[u] = *reinterpret_cast<const uint4*>(base + ((size_t)j * a.H + c * 8) * 2);
+      for (int u = 0; u < kQuads; ++u) {
+        const int q = q0 + u * kThreads + (int)threadIdx.x;
+        if (q < nquad) v[u] = *reinterpret_cast<const uint2*>(base + ((size_t)j * a.H + q * 4) * 2);
       }
 #pragma unroll
-      for (int u = 0; u < kChunks; ++u) {
-        const int c = c0 + u * kThreads + (int)threadIdx.x;
-        if (c >= nchunk) continue;
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int u = 0; u < kQuads; ++u) {
+        const int q = q0 + u * kThreads + (int)threadIdx.x;
+        if (q >= nquad) continue;
+        const uint32_t bits[4] = {v[u].x & 0xFFFFu, v[u].x >> 16, v[u].y & 0xFFFFu, v[u].y >> 16};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t bits = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-          const float f = __uint_as_float(bits << 16);
+        for (int i = 0; i < 4; ++i) {
+          const float f = __uint_as_float(bits[i] << 16);
           if (local) {
             y[u][i] += f;
             if (audit) {
-              if (bits == 0xFFFFu) unwritten |= 1 << j;
-              else if (!isfinite(f)) nonfinite |= 1 << j;
+              if (bits[i] == 0xFFFFu) unwritten |= 1u << j;
+              else if (!isfinite(f)) nonfinite |= 1u << j;
             }
-          } else if (bits != 0xFFFFu) {
-            clobbered |= 1 << j;
+          } else if (bits[i] != 0xFFFFu) {
+            clobbered |= 1u << j;
           }
         }
       }
@@ -78,25 +79,26 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
     if (yrow) {   // streamed out: not re-read here
       typedef float f32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int u = 0; u < kChunks; ++u) {
-        const int c = c0 + u * kThreads + (int)threadIdx.x;
-        if (c >= nchunk) continue;
-        f32x4* dst = reinterpret_cast<f32x4*>(yrow + c * 8);
-        __builtin_nontemporal_store(f32x4{y[u][0], y[u][1], y[u][2], y[u][3]}, dst);
-        __builtin_nontemporal_store(f32x4{y[u][4], y[u][5], y[u][6], y[u][7]}, dst + 1);
+      for (int u = 0; u < kQuads; ++u) {
+        const int q = q0 + u * kThreads + (int)threadIdx.x;
+        if (q < nquad)
+          __builtin_nontemporal_store(f32x4{y[u][0], y[u][1], y[u][2], y[u][3]},
+                                      reinterpret_cast<f32x4*>(yrow + q * 4));
       }
     }
   }
   if (audit) {
-    // per-slot flags (bit j), merged over the workgroup, then counted
-    atomicOr(&s_cnt[0], unwritten);
-    atomicOr(&s_cnt[1], clobbered);
-    atomicOr(&s_cnt[2], nonfinite);
+    // per-slot flags, merged over the workgroup, then counted
+    if (threadIdx.x < 3) s_flag[threadIdx.x] = 0;
+    __syncthreads();
+    if (unwritten) atomicOr(&s_flag[0], (int)unwritten);
+    if (clobbered) atomicOr(&s_flag[1], (int)clobbered);
+    if (nonfinite) atomicOr(&s_flag[2], (int)nonfinite);
     __syncthreads();
     if (threadIdx.x == 0) {
-      if (s_cnt[0]) atomicAdd(a.report + 0, __popc(s_cnt[0]));
-      if (s_cnt[1]) atomicAdd(a.report + 1, __popc(s_cnt[1]));
-      if (s_cnt[2]) atomicAdd(a.report + 2, __popc(s_cnt[2]));
+      if (s_flag[0]) atomicAdd(a.report + 0, __popc(s_flag[0]));
+      if (s_flag[1]) atomicAdd(a.report + 1, __popc(s_flag[1]));
+      if (s_flag[2]) atomicAdd(a.report + 2, __popc(s_flag[2]));
     }
   }
 }
