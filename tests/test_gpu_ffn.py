@@ -240,6 +240,53 @@ def test_combine_check_reduce_and_audit():
     assert report.cpu().tolist()[:2] == [1, 1]
 
 
+def test_combine_check_two_passes_and_every_audit_flag():
+    # H = 9216: the reduction walks the row in two passes (8192 elements per
+    # pass); y_local must be, bit for bit, the fp32 sum in ascending slot
+    # order of the bf16 rows the kernel wrote, and within the bar of the
+    # oracle; faults planted past element 8192 must raise each audit count
+    wl = _small_wl(hidden=9216, inter=128, num_slices=3, tokens_per_slice=20, num_experts=16,
+                   top_k=4, num_local=5, seed=4711)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=16)
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    _route_and_layout(ffn, up)
+    up.reset_combine()
+    run_forward(ffn, up)
+    y = torch.full((wl.num_tokens, wl.hidden), float("nan"), dtype=torch.float32, device=dev())
+    report = torch.zeros(4, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, y=y, report=report)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    assert report.cpu().tolist() == [0, 0, 0, 0]
+    bits = up.combine_bits()
+    vals = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    want = np.zeros((wl.num_tokens, wl.hidden), dtype=np.float32)
+    for j in range(wl.top_k):
+        loc = ref.written[:, j]
+        want[loc] = want[loc] + vals[loc, j]
+    got = y.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    has = ref.written.any(axis=1)
+    assert has.any() and (~ref.written).any()
+    assert row_rel_err(got.astype(np.float64), ref.y_local)[has].max() <= TOL_BF16
+    # plant, all past the first pass: a non-local slot written, a local slot
+    # with one element left at the sentinel, another local slot holding +inf
+    S_T = wl.tokens_per_slice
+    loc = np.argwhere(ref.written)
+    nl = np.argwhere(~ref.written)[0]
+    assert len(loc) >= 2
+    a, b = loc[0], loc[-1]
+    up.comb_all[nl[0] // S_T, nl[0] % S_T, nl[1], 9000] = 0
+    up.comb_all[a[0] // S_T, a[0] % S_T, a[1], 8200] = SENTINEL
+    up.comb_all[b[0] // S_T, b[0] % S_T, b[1], 9215] = 0x7F80   # bf16 +inf
+    report.zero_()
+    ffn.combine_check(up.comb_slices, y=None, report=report)
+    torch.cuda.synchronize()
+    assert report.cpu().tolist() == [1, 1, 1, 0]
+
+
 def test_abi_maximum_sizes():
     # every table at its ABI limit: 64 source slices (MOE_MAX_SLICES), 1024
     # global experts (16 logits per lane of the routing wavefront), top-16,
