@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
 #define MOE_TRACE_WORDS 10      /* uint32 words per task record */
@@ -224,17 +224,23 @@ int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
  *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
  *   y_local        [N, H] fp32 or NULL: y_local[n] = sum over the local
  *                  slots j of token n, in ascending j, of combine[n, j].
+ *   status         device int32 or NULL: the status word the FFN calls
+ *                  wrote (moe_sched_params.status), read on the stream after
+ *                  them.
  *   report         device int32 [4] or NULL; slot counts are ADDED to it:
  *                  [0] local slots with an element still holding the
  *                      sentinel 0xFFFF (not fully written),
  *                  [1] non-local slots with an element that is not the
  *                      sentinel (written although not local),
  *                  [2] local slots holding a non-finite value,
- *                  [3] unused (0).
- *                  The audit reads every slot; pass NULL to skip it. */
+ *                  [3] receives *status (MOE_OK, or MOE_ERR_TIMEOUT when a
+ *                      Linear-2 tile gave up waiting and left its rows
+ *                      unwritten) when status is given; unchanged otherwise.
+ *                  The audit reads every slot; pass NULL to skip it.
+ * Neither the status word nor the report is cleared by the library. */
 int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,
                           void* const* combine_slices, float* y_local,
-                          int32_t* report, void* stream);
+                          const int32_t* status, int32_t* report, void* stream);
 
 /* One schedule configuration and what the planner's model predicts for it. */
 typedef struct {

@@ -17,7 +17,7 @@ from ._lib import (MOE_BF16, MOE_FP8_E4M3, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTE
                    MoeError, MoeLayout, MoePlan, MoeSchedParams, MoeShape)
 
 __all__ = ["MoeExpertFFN", "LayoutBuffers", "MoeError", "SCHEDULES", "make_shape", "prediction_dict",
-           "make_params", "library"]
+           "make_params", "library", "check_layout_inputs", "check_combine_inputs"]
 
 SCHEDULES = {"expert_wave": MOE_SCHED_EXPERT_WAVE, "interleaved": MOE_SCHED_INTERLEAVED}
 SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
@@ -53,6 +53,55 @@ def make_params(schedule="interleaved", lead_d=0, experts_per_wave=0, grid=0, ti
                           None if status is None else status.data_ptr(),
                           None if trace is None else trace.data_ptr(), trace_capacity,
                           debug_skip_l1_row)
+
+
+def _need(t, what, nbytes, dtype=None, device_type="cuda"):
+    """``t`` must be a contiguous tensor on ``device_type`` of at least
+    ``nbytes`` bytes (and of ``dtype`` when given). The C ABI takes raw
+    pointers, so a wrong tensor would let a kernel read or write past its
+    end; this raises ValueError before anything is enqueued."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: need dtype {dtype}, got {t.dtype}")
+    if t.device.type != device_type or not t.is_contiguous():
+        raise ValueError(f"{what}: need a contiguous {device_type} tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: need at least {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
+def check_layout_inputs(shape: MoeShape, logits=None, bias=None, topk_idx=None, topk_w=None,
+                        device_type="cuda"):
+    """Routing inputs of moe_dispatch_layout: fp32 logits [N, E] and an
+    optional fp32 bias [E], or (without logits) int32 topk_idx and fp32
+    topk_w [N, k]."""
+    N = shape.num_slices * shape.tokens_per_slice
+    E, k = shape.num_experts, shape.top_k
+    if logits is not None:
+        _need(logits, "logits", N * E * 4, torch.float32, device_type)
+        if bias is not None:
+            _need(bias, "expert bias", E * 4, torch.float32, device_type)
+    else:
+        if bias is not None:
+            raise ValueError("an expert bias needs logits (it enters the routing)")
+        _need(topk_idx, "topk_idx", N * k * 4, torch.int32, device_type)
+        _need(topk_w, "topk_w", N * k * 4, torch.float32, device_type)
+
+
+def check_combine_inputs(shape: MoeShape, combine_slices, y=None, report=None, device_type="cuda"):
+    """Buffers of moe_combine_check: S combine slices of [T, k, H] 2-byte
+    (bf16) elements, an optional fp32 y_local [N, H] and int32 report [4]."""
+    S, T, k, H = shape.num_slices, shape.tokens_per_slice, shape.top_k, shape.hidden
+    if len(combine_slices) != S:
+        raise ValueError(f"need {S} combine slices, got {len(combine_slices)}")
+    for t in combine_slices:
+        if t is not None and t.element_size() != 2:
+            raise ValueError("combine slices hold 2-byte (bf16) elements")
+        _need(t, "combine slice", T * k * H * 2, None, device_type)
+    if y is not None:
+        _need(y, "y_local", S * T * H * 4, torch.float32, device_type)
+    if report is not None:
+        _need(report, "report", 16, torch.int32, device_type)
 
 
 def _stream(stream):
@@ -135,6 +184,7 @@ class MoeExpertFFN:
         """Routing (from fp32 logits [N, E] and optional bias [E]) or given
         top-k (int32 idx and fp32 weights [N, k]), then the dispatch layout."""
         lb = self.layout_bufs
+        check_layout_inputs(self.shape, logits, bias, topk_idx, topk_w, self.device.type)
         if logits is None:
             lb.topk_idx.copy_(topk_idx)
             lb.topk_w.copy_(topk_w)
@@ -168,7 +218,8 @@ class MoeExpertFFN:
         def need(t, nbytes, what):
             if t is None:
                 raise ValueError(f"{what} is required")
-            if not t.is_cuda or t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+            if (t.device.type != self.device.type or t.numel() * t.element_size() < nbytes
+                    or not t.is_contiguous()):
                 raise ValueError(f"{what}: need a contiguous device tensor of at least {nbytes} bytes")
 
         if len(x_slices) != S or len(combine_slices) != S:
@@ -218,7 +269,25 @@ class MoeExpertFFN:
                          self.plan.workspace_bytes, params, _stream(stream))
 
     def combine_check(self, combine_slices, y=None, report=None, stream=None):
+        """Source-side reduction of the local slots into ``y`` (fp32 [N, H])
+        and, with ``report`` (int32 [4]), the sentinel audit; report[3]
+        receives this instance's device status word."""
+        check_combine_inputs(self.shape, combine_slices, y, report, self.device.type)
         _lib.combine_check(self.shape, self.layout_bufs.c_struct(),
                            [t.data_ptr() for t in combine_slices],
-                           None if y is None else y.data_ptr(),
+                           None if y is None else y.data_ptr(), self.status.data_ptr(),
                            None if report is None else report.data_ptr(), _stream(stream))
+
+    def check_status(self, clear: bool = True) -> None:
+        """Raise MoeError if a kernel of an earlier call recorded an error in
+        the device status word (a Linear-2 tile that gave up waiting for its
+        Linear-1 inputs leaves its combine rows unwritten). The library never
+        clears the word, so one error stays latched until it is read here:
+        ``clear`` resets it. Waits for the device first, as the word is only
+        meaningful once the calls that write it have completed."""
+        torch.cuda.synchronize(self.device)
+        st = int(self.status.item())
+        if st != 0:
+            if clear:
+                self.status.zero_()
+            raise MoeError(st, "device status")

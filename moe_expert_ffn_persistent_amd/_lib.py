@@ -114,7 +114,7 @@ def load(path: str | None = None):
                                     c_vp, c_vp, P(c_vp), c_vp, ctypes.c_size_t,
                                     P(MoeSchedParams), c_vp]
     lib.moe_combine_check.restype = c_i32
-    lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp]
+    lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp, c_vp]
     lib.moe_store_burst_probe.restype = c_i32
     lib.moe_store_burst_probe.argtypes = [P(MoeBurstParams), c_vp, ctypes.c_size_t, c_vp, c_vp]
     lib.moe_predict_schedule.restype = c_i32
@@ -172,9 +172,9 @@ def ffn_forward(shape, layout, x_ptrs, xs_ptrs, w1, w1s, w2, w2s, comb_ptrs, ws,
                                  ctypes.byref(params), stream), "moe_ffn_forward")
 
 
-def combine_check(shape, layout, comb_ptrs, y_ptr, report_ptr, stream):
+def combine_check(shape, layout, comb_ptrs, y_ptr, status_ptr, report_ptr, stream):
     check(load().moe_combine_check(ctypes.byref(shape), ctypes.byref(layout),
-                                   ptr_array(comb_ptrs), y_ptr, report_ptr, stream),
+                                   ptr_array(comb_ptrs), y_ptr, status_ptr, report_ptr, stream),
           "moe_combine_check")
 
 

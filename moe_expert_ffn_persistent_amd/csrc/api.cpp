@@ -374,7 +374,7 @@ int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* c
 }
 
 int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, float* y,
-                          int32_t* report, void* stream) {
+                          const int32_t* status, int32_t* report, void* stream) {
   if (!shape_ok(s) || !lay || !lay->pair_row || !comb) return MOE_ERR_INVALID_ARG;
   CheckArgs a{};
   a.S = s->num_slices;
@@ -388,6 +388,7 @@ int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const
   }
   a.pair_row = lay->pair_row;
   a.y = y;
+  a.status = status;
   a.report = report;
   return launch_check(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

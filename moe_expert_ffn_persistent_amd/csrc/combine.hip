@@ -8,6 +8,9 @@
 // caller filled them with: every local slot must have been written, and no
 // other slot may have been touched.
 //
+// With a report, the status word the FFN calls wrote is copied into report[3]
+// by the first workgroup (one workgroup runs even for an empty batch).
+//
 // One workgroup of eight wavefronts per token. Each wavefront reads the
 // token's k row indices itself and ballots them into the local-slot mask, so
 // no LDS or barrier precedes the data loads. Each thread owns quads of 4
@@ -29,6 +32,10 @@ constexpr int kQuads = 4;   // quads per thread in flight (H <= 8192 in one pass
 __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
   __shared__ int s_flag[3];   // unwritten, clobbered, nonfinite slots (bit j)
   const int n = blockIdx.x;
+  if (n == 0 && threadIdx.x == 0 && a.report && a.status)
+    __hip_atomic_store(a.report + 3, __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n >= a.S * a.T) return;
   const int s = n / a.T;
   const int t = n - s * a.T;
   const int lane = threadIdx.x & 63;
@@ -113,7 +120,8 @@ __global__ void zero_words(uint32_t* p, size_t words) {
 
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream) {
   const int N = a.S * a.T;
-  if (N > 0) combine_check<<<N, kThreads, 0, stream>>>(a);
+  const int blocks = N > 0 ? N : (a.report && a.status ? 1 : 0);
+  if (blocks > 0) combine_check<<<blocks, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -97,6 +97,7 @@ struct CheckArgs {
   void* comb[MOE_MAX_SLICES];
   const int32_t* pair_row;
   float* y;
+  const int32_t* status;   // FFN status word or nullptr (copied to report[3])
   int32_t* report;
 };
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);

@@ -8,11 +8,14 @@
 // walks its own task stream; every quantity here is uniform across the
 // workgroup and is kept in scalar registers.
 //
-// Interleaved order (X-Stage paper, section 4.2, Algorithm 1): two cursors
-// k1 (Linear-1) and k2 (Linear-2) start at g and advance by G; the Linear-2
-// tile at k2 is taken when p2 + D <= p1 (p1 counts as unbounded once the
-// Linear-1 stream is exhausted), else the Linear-1 tile at k1. The paper's
-// paired-CTA role is dropped: CDNA4 has no CTA pairs, so n = k mod N_i.
+// Interleaved order (X-Stage paper, section 4.2, Algorithm 1): workgroup g
+// owns the Linear-1 tiles and the Linear-2 tiles whose global index (row p
+// times the N-tiles per row, plus n) is g modulo G, and runs each kind in
+// ascending index. The two kinds are merged on the fly by the lead rule: the
+// next own Linear-2 tile, of row p2, is due once the next own Linear-1 tile
+// lies at row p2 + D or beyond, or none is left. Two cursors walk the own
+// indices (start g, step G). CDNA4 has no CTA pairs, so the paper's paired
+// role is dropped and n = k mod N_i.
 //
 // Expert-Wave order (X-Stage paper, section 2.2 and Figure 4(a)): waves of
 // consecutive local experts; within a wave, the Linear-1 stream, then the
@@ -49,13 +52,14 @@ struct InterleavedStream {
   __host__ __device__ Task next() {
     const int t1 = P * N1, t2 = P * N2;
     if (k1 >= t1 && k2 >= t2) return Task{0, 0, 0};
-    // p1 is unbounded once the Linear-1 stream is exhausted: the Linear-2
-    // tile is then taken whatever the lead (a lead near INT_MAX must not
-    // turn the comparison around and hand out a Linear-1 tile past the end)
+    // the Linear-2 tile is due when no own Linear-1 tile is left (whatever
+    // the lead: a lead near INT_MAX must not turn the comparison around and
+    // hand out a Linear-1 tile past the end) or the next one is D rows ahead
     const bool l1_done = k1 >= t1;
     const int p1 = l1_done ? 0 : k1 / N1;
     const int p2 = k2 / N2;
-    if (k2 < t2 && (l1_done || (long long)p2 + D <= (long long)p1)) {
+    const bool l2_due = k2 < t2 && (l1_done || (long long)p2 + D <= (long long)p1);
+    if (l2_due) {
       Task t{2, p2, k2 - p2 * N2};
       k2 += G;
       return t;

@@ -47,7 +47,7 @@ __all__ = [
     "bf16_bits_to_f64", "e4m3_to_f64", "e2m1_to_f64", "e8m0_to_f64", "unpack_e2m1",
     "dequant_blocks", "dequant_mx", "route", "Layout",
     "dispatch_layout", "swiglu", "expert_ffn", "combine", "local_reduce",
-    "OracleResult", "run", "scheduler_rows",
+    "OracleResult", "run",
 ]
 
 
@@ -183,11 +183,6 @@ def dispatch_layout(idx: np.ndarray, e0: int, L: int, block_m: int) -> Layout:
     pair_row = np.full(flat.size, -1, dtype=np.int32)
     pair_row[row_pair] = np.arange(row_pair.size, dtype=np.int32)
     return Layout(counts, row_offset, tile_offset, row_pair, pair_row, block_m)
-
-
-def scheduler_rows(counts, block_m: int) -> int:
-    """P = sum_e ceil(M_e / b_m)."""
-    return int(sum((int(c) + block_m - 1) // block_m for c in counts))
 
 
 # ---------------------------------------------------------------------------

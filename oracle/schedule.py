@@ -9,27 +9,30 @@ N-tile n of the hidden output, N2 tiles per row). Scheduler rows p are the
 M-blocks of all local experts laid end to end, expert e owning rows
 O_e .. O_{e+1}-1 (X-Stage paper, Algorithm 1 legend).
 
-Interleaved order (X-Stage paper, section 4.2, Algorithm 1): instance g keeps
-two cursors k1 and k2, both starting at g and advancing by the instance count
-G. Row p_i = floor(k_i / N_i). It emits the Linear-2 tile at k2 when that
-stream is not finished and p2 + D <= p1, where p1 is taken as +infinity once
-the Linear-1 stream is finished; otherwise it emits the Linear-1 tile at k1.
-The paired-CTA role r of the paper is dropped (one instance per tile), so the
-N-tile index is simply k mod N_i.
+Both orders are written here from the properties the pages state, not as a
+cursor machine, so that they check the kernel's stream code (which is one)
+from another direction:
+
+Interleaved order (X-Stage paper, section 4.2, Algorithm 1): instance g owns
+the Linear-1 tiles whose global index k = p*N1 + n is g modulo G and the
+Linear-2 tiles whose index k = p*N2 + n is g modulo G, and runs each kind in
+ascending index. The two kinds are merged by the lead rule: a Linear-2 tile
+of row p goes ahead of the instance's next Linear-1 tile exactly when that
+tile's row is at least p + D (or no Linear-1 tile is left). The paired-CTA
+role of the paper is dropped (one instance per tile), so n = k mod N_i.
 
 Expert-Wave order (section 2.2; Figure 4(a)): local experts are grouped into
-waves; the wave's Linear-1 tiles run, then its Linear-2 tiles, then the next
-wave. Within each wave, each of the two tile streams is walked the way
-Algorithm 1 walks its streams (cursor starts at g and advances by G; the
+waves; all Linear-1 tiles of a wave run, then its Linear-2 tiles, then the
+next wave. The tiles of one wave and kind are enumerated row by row, N-tile by
+N-tile, and instance g takes every G-th of them starting at the g-th (the
 persistent tile visitor of the resource-management paper, section C, takes
 tiles b, b+G, b+2G, ... the same way). With one wave holding every row this
 is exactly Algorithm 1 with a lead D >= P. The wave size is not given on the
 pages; the reading taken here closes a wave, in local-expert order, as soon
-as it holds at least G Linear-1 tiles (one tile for every instance).
+as it holds at least G Linear-1 tiles (one tile for every instance); the
+last wave takes the rest.
 """
 from __future__ import annotations
-
-import math
 
 L1, L2 = 1, 2
 
@@ -46,50 +49,56 @@ def expert_of_row(tile_offset, p: int) -> int:
 
 
 def waves_greedy(tile_offset, N1: int, G: int, experts_per_wave: int = 0):
-    """Wave boundaries as scheduler-row ranges [(r0, r1), ...]. With
-    experts_per_wave > 0, waves take that many experts each; otherwise a wave
-    closes once it holds >= G Linear-1 tiles. Experts with no rows are skipped
-    over (they add no rows). The last wave takes whatever is left."""
+    """Wave boundaries as scheduler-row ranges [(r0, r1), ...]. The local
+    experts are cut into consecutive groups: groups of experts_per_wave
+    experts when that is positive (the last group takes what is left);
+    otherwise each group runs from its first expert to the first expert at
+    which the group's Linear-1 tile count, N1 times its rows, reaches G, or
+    to the last expert. Groups without rows are dropped."""
     L = len(tile_offset) - 1
-    waves = []
-    start = tile_offset[0]
-    n_exp = 0
-    for e in range(L):
-        n_exp += 1
-        r1 = tile_offset[e + 1]
-        full = (n_exp >= experts_per_wave) if experts_per_wave > 0 else ((r1 - start) * N1 >= G)
-        if full or e == L - 1:
-            if r1 > start:
-                waves.append((start, r1))
-            start = r1
-            n_exp = 0
-    return waves
+    groups = []                        # [first expert, one past the last expert)
+    a = 0
+    while a < L:
+        if experts_per_wave > 0:
+            b = min(L, a + experts_per_wave)
+        else:
+            full = [e + 1 for e in range(a, L) if (tile_offset[e + 1] - tile_offset[a]) * N1 >= G]
+            b = full[0] if full else L
+        groups.append((a, b))
+        a = b
+    return [(tile_offset[a], tile_offset[b]) for a, b in groups if tile_offset[b] > tile_offset[a]]
+
+
+def _phase_tiles(kind: int, r0: int, r1: int, N: int):
+    """The tiles of one kind over rows r0..r1-1, row by row, N-tile by N-tile."""
+    return [(kind, p, n) for p in range(r0, r1) for n in range(N)]
 
 
 def expert_wave_stream(g: int, G: int, waves, N1: int, N2: int):
-    """Tasks of instance g under the Expert-Wave order."""
+    """Tasks of instance g under the Expert-Wave order: per wave, every G-th
+    Linear-1 tile from the g-th, then every G-th Linear-2 tile from the g-th."""
     seq = []
     for (r0, r1) in waves:
-        rows = r1 - r0
-        seq += [(L1, r0 + t // N1, t % N1) for t in range(g, rows * N1, G)]
-        seq += [(L2, r0 + t // N2, t % N2) for t in range(g, rows * N2, G)]
+        seq += _phase_tiles(L1, r0, r1, N1)[g::G]
+        seq += _phase_tiles(L2, r0, r1, N2)[g::G]
     return seq
 
 
 def interleaved_stream(g: int, G: int, P: int, N1: int, N2: int, D: int):
-    """Tasks of instance g under Algorithm 1."""
+    """Tasks of instance g under Algorithm 1: the instance's own Linear-1 and
+    Linear-2 tiles (every G-th from the g-th, ascending), merged so that each
+    Linear-2 tile of row p follows exactly the own Linear-1 tiles of rows
+    below p + D that precede it in ascending order."""
+    own1 = _phase_tiles(L1, 0, P, N1)[g::G]
+    own2 = _phase_tiles(L2, 0, P, N2)[g::G]
     out = []
-    k1 = k2 = g
-    while k1 < P * N1 or k2 < P * N2:
-        p1 = k1 // N1 if k1 < P * N1 else math.inf
-        p2 = k2 // N2
-        if k2 < P * N2 and p2 + D <= p1:
-            out.append((L2, p2, k2 % N2))
-            k2 += G
-        else:
-            out.append((L1, p1, k1 % N1))
-            k1 += G
-    return out
+    i = 0
+    for t2 in own2:
+        while i < len(own1) and own1[i][1] < t2[1] + D:
+            out.append(own1[i])
+            i += 1
+        out.append(t2)
+    return out + own1[i:]
 
 
 def d_knee(block_n: int, instances: int, inter: int) -> int:

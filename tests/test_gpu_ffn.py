@@ -202,8 +202,20 @@ def test_watchdog_reports_timeout_instead_of_hanging():
     run_forward(ffn, up, debug_skip_l1_row=0, timeout_ms=50)
     torch.cuda.synchronize()
     assert int(ffn.status.item()) == -5
+    # the audit sees the status word (report[3]) and the rows the timed-out
+    # Linear-2 tiles left at the sentinel (report[0])
+    report = torch.zeros(4, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, report=report)
+    torch.cuda.synchronize()
+    rep = report.cpu().tolist()
+    assert rep[3] == -5 and rep[0] > 0 and rep[1] == 0, rep
+    # check_status raises and clears the latched word
+    with pytest.raises(_lib.MoeError) as err:
+        ffn.check_status()
+    assert err.value.status == -5
+    assert int(ffn.status.item()) == 0
+    ffn.check_status()
     # the workspace is clean again: a normal call afterwards is correct
-    ffn.status.zero_()
     up.reset_combine()
     run_forward(ffn, up)
     torch.cuda.synchronize()
@@ -327,7 +339,11 @@ def test_empty_batch_and_single_token():
     up = Uploaded(mi.make_inputs(wl))
     ffn.layout(logits=up.logits)
     run_forward(ffn, up)
+    # an empty batch still reports the status word
+    report = torch.full((4,), 7, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, report=report)
     torch.cuda.synchronize()
+    assert report.cpu().tolist() == [7, 7, 7, 0]
     wl1 = _small_wl(num_slices=1, tokens_per_slice=1, num_local=32, seed=31)
     inp = mi.make_inputs(wl1)
     ref = mo.run(inp, block_m=16)

@@ -35,6 +35,38 @@ def test_alg1_hand_trace():
         assert sc.interleaved_stream(g, G, P, N1, N2, D) == streams[g]
 
 
+def _read_wave_fixture():
+    cases = []
+    for line in open(os.path.join(GOLDEN, "expert_wave_small.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("params"):
+            prm = dict(kv.split("=") for kv in line.split()[1:])
+            cases.append({"tile_offset": [int(v) for v in prm["tile_offset"].split(",")],
+                          "N1": int(prm["N1"]), "N2": int(prm["N2"]), "G": int(prm["G"]),
+                          "epw": int(prm["experts_per_wave"]), "streams": {}})
+        elif line.startswith("waves"):
+            cases[-1]["waves"] = [tuple(int(v) for v in w.split("-")) for w in line.split()[1:]]
+        else:
+            g, rest = line.split(":")
+            cases[-1]["streams"][int(g)] = [_parse_task(t) for t in rest.split()]
+    return cases
+
+
+def test_expert_wave_multi_wave_hand_trace():
+    # three waves, an expert without rows, a partial last wave; greedy and
+    # fixed-size grouping (X-Stage paper, section 2.2, Figure 4(a))
+    cases = _read_wave_fixture()
+    assert len(cases) == 2
+    for c in cases:
+        waves = sc.waves_greedy(c["tile_offset"], c["N1"], c["G"], c["epw"])
+        assert waves == c["waves"]
+        streams = sc.all_streams("expert_wave", c["G"], c["tile_offset"], c["N1"], c["N2"],
+                                 experts_per_wave=c["epw"])
+        assert streams == [c["streams"][g] for g in range(c["G"])]
+
+
 def test_dknee_fixture():
     for line in open(os.path.join(GOLDEN, "dknee.txt")):
         if line.startswith("#") or not line.strip():
