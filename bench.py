@@ -8,11 +8,12 @@ y_local). Inputs are resident in HBM before the timed region starts.
 
 Prints one JSON line. ``value`` is TFLOP/s of the algorithmic FLOPs
 (6*H*I per routed row) over the whole step, for the schedule named in
-config.schedule; per-schedule FFN-only timings (paired, A-B-C-C-B-A order,
-for Expert-Wave, Interleaved and the schedule planner's recommendation, with
-the planner's predictions beside them) and the roofline of the dominant
-kernel ride along, with the CPU oracle timed on a bounded sample of the same
-workload.
+config.schedule; per-schedule FFN-only timings (paired, A-B-C-D-D-C-B-A
+order, for Expert-Wave with the automatic waves and with one wave,
+Interleaved and the schedule planner's recommendation, with the planner's
+predictions beside them), the mean shader clock over the mainloops (from the
+kernel's task trace) and the roofline of the dominant kernel ride along, with
+the CPU oracle (float32) timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -70,41 +71,87 @@ def algorithmic_counts(wl, R: int, active: int):
         weights=weight_bytes, x=x_bytes, h=h_bytes, combine=comb_bytes, scales=scale_bytes)
 
 
-def cpu_baseline(inp, seconds_budget: float):
-    """Time the CPU oracle on a bounded sample: routing and layout over all
-    tokens, then the expert FFN and weighted combine for as many local
-    experts (in order) as fit the budget. When every local expert fits, the
-    whole workload is run again while the budget lasts and the median time
-    is reported."""
+def host_info() -> dict:
+    """CPU model, BLAS vendor and the threads BLAS runs with."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"cpu_model": model,
+            "blas": ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or "unknown",
+            "threads": max([i.get("num_threads", 1) for i in blas] or [1]),
+            "affinity_cores": len(os.sched_getaffinity(0))}
 
+
+def cpu_baseline(inp, seconds_budget: float):
+    """Time the CPU oracle (its float32 setting: the same code in single
+    precision) on a bounded sample: routing and layout over all tokens, then
+    the expert FFN and weighted combine for as many local experts (in order)
+    as fit the budget. When every local expert fits, the whole workload is
+    run again while the budget lasts and the median time is reported."""
     from oracle import moe_oracle as mo
     wl = inp.wl
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = host_info()
     t0 = time.perf_counter()
     n_exp = 0
     rows = 0
-    res = None
     while n_exp < wl.num_local:
         n_exp = min(wl.num_local, max(1, n_exp * 2))
         t1 = time.perf_counter()
-        res = mo.run(inp, block_m=128, experts=n_exp)
+        res = mo.run(inp, block_m=128, experts=n_exp, float_type=np.float32)
         dt = time.perf_counter() - t1
         rows = int(res.layout.row_offset[n_exp])
+        del res
         if time.perf_counter() - t0 + 2.5 * dt > seconds_budget:
             break
     times = [dt]
     while n_exp == wl.num_local and time.perf_counter() - t0 + 1.2 * dt < seconds_budget:
         t1 = time.perf_counter()
-        mo.run(inp, block_m=128, experts=n_exp)
+        mo.run(inp, block_m=128, experts=n_exp, float_type=np.float32)
         times.append(time.perf_counter() - t1)
     dt = statistics.median(times)
     flops = 6.0 * wl.hidden * wl.inter * rows
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(info["threads"]),
             "kind": "oracle",
             "sample": f"{wl.name}: routing+layout of all {wl.num_tokens} tokens, expert FFN and "
-                      f"combine of local experts 0..{n_exp - 1} ({rows} routed rows), float64 "
-                      f"numpy, {dt:.2f} s (median of {len(times)})"}
+                      f"combine of local experts 0..{n_exp - 1} ({rows} routed rows), float32 "
+                      f"numpy, {dt:.2f} s (median of {len(times)})",
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
+            "affinity_cores": info["affinity_cores"]}
+
+
+def trace_clock(ffn, call, wall_khz: int):
+    """Mean shader clock (MHz) over the mainloops of one traced FFN call:
+    shader-clock cycles (trace words 6..7) over wall-clock ticks (words 2..4)
+    of every task."""
+    import torch
+    from moe_expert_ffn_persistent_amd import _lib
+    cap = 512
+    tr = torch.zeros((ffn.plan.grid, cap, _lib.TRACE_WORDS), dtype=torch.int32, device=ffn.device)
+    call(trace=tr, trace_capacity=cap)
+    torch.cuda.synchronize()
+    t = tr.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    t = t.reshape(-1, _lib.TRACE_WORDS)
+    t = t[t[:, 0] != 0]
+    cyc = (t[:, 7] - t[:, 6]) & 0xFFFFFFFF
+    wall = (t[:, 4] - t[:, 2]) & 0xFFFFFFFF
+    ok = wall > 0
+    if not ok.any():
+        return None
+    return round(float(cyc[ok].sum()) / float(wall[ok].sum()) * wall_khz / 1e3, 1)
+
+
+def rocm_version() -> str:
+    try:
+        return open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        return "unknown"
 
 
 def main():
@@ -112,7 +159,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3", choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--workload", default="dsv3_skew", choices=sorted(mi.WORKLOADS),
+                    help="default: the largest single-GPU configuration by FLOPs (the "
+                         "DeepSeek-V3-shaped share with Zipf-skewed routing, 8 x 2048 tokens)")
     ap.add_argument("--schedule", default="interleaved", choices=["interleaved", "expert_wave", "auto"],
                     help="auto: the schedule planner's recommendation for the workload's routing, "
                          "resolved once before the timed region")
@@ -121,7 +170,7 @@ def main():
     ap.add_argument("--tokens-per-slice", type=int, default=0,
                     help="run the workload's shapes at another batch size (workload name gets @T<n>)")
     ap.add_argument("--lead-d", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -193,8 +242,7 @@ def main():
     for _ in range(args.warmup):
         step(head_cfg)
     torch.cuda.synchronize()
-    if int(ffn.status.item()) != 0:
-        raise RuntimeError(f"device status {int(ffn.status.item())} after warm-up")
+    ffn.check_status()   # raises on a latched device error
 
     # ---- timed region: exactly K steps of the headline schedule ----
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -207,20 +255,23 @@ def main():
     wall = time.perf_counter() - t0
     ffn_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = wall * 1e3 / args.steps
-    if int(ffn.status.item()) != 0:
-        raise RuntimeError(f"device status {int(ffn.status.item())} in the timed region")
+    ffn.check_status()
 
     # ---- paired schedule comparison, FFN only, A-B-C-C-B-A: both orders
     # with their default parameters, and the planner's recommendation ----
     arms = {"expert_wave": {"schedule": "expert_wave"}, "interleaved": {"schedule": "interleaved"},
+            "expert_wave_one_wave": {"schedule": "expert_wave", "experts_per_wave": wl.num_local},
             "recommended": rec_cfg}
     # the recommendation is timed as an arm of its own only when it is not
-    # one of the two default configurations
+    # one of the fixed configurations (Expert-Wave with one wave is a
+    # planner candidate too)
     same_as = None
     if rec_cfg["schedule"] == "interleaved" and rec_cfg["lead_d"] == ffn.plan.lead_d:
         same_as = "interleaved"
     elif rec_cfg["schedule"] == "expert_wave" and rec_cfg["experts_per_wave"] == 0:
         same_as = "expert_wave"
+    elif rec_cfg["schedule"] == "expert_wave" and rec_cfg["experts_per_wave"] >= wl.num_local:
+        same_as = "expert_wave_one_wave"
     if same_as:
         del arms["recommended"]
     per = {a: [] for a in arms}
@@ -244,6 +295,9 @@ def main():
                          "hbm_gbs": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
     speedup = (statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
                if per["interleaved"] else None)
+    best_wave = min(statistics.median(per["expert_wave"]), statistics.median(per["expert_wave_one_wave"]))
+    speedup_best = best_wave / statistics.median(per["interleaved"])
+    sclk = trace_clock(ffn, lambda **kw: ffn_call(dict(head_cfg, **kw)), ffn.plan.wall_clock_khz)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -307,8 +361,13 @@ def main():
                    "r_expert": round(max_rows / (wl.num_tokens * k / wl.num_experts), 3)},
         "pct_of_mfma_peak": round(100 * flops / (ms_per_step * 1e-3) / 1e12 / peak_flops, 2),
         "ffn_only_ms": round(statistics.mean(ffn_ms), 4),
+        "ffn_ms_p50_p90": [round(float(np.percentile(ffn_ms, 50)), 4), round(float(np.percentile(ffn_ms, 90)), 4)],
         "per_schedule": sched_out,
         "speedup_interleaved_over_wave": None if speedup is None else round(speedup, 4),
+        "speedup_interleaved_over_best_wave": round(speedup_best, 4),
+        "sclk_mhz_mainloop": sclk,
+        "rocm": rocm_version(),
+        "torch": torch.__version__,
         "planner": {
             "recommended": rec_cfg,
             "predicted_units": {"expert_wave": round(pred["candidates"][0]["makespan"], 1),

@@ -207,7 +207,7 @@ def combine(w: np.ndarray, layout: Layout, Y: np.ndarray, N: int, k: int, H: int
     """Weighted combine stores: slot (n, j) of the combine buffer receives
     w[n, j] * Y[row(n*k + j)] when pair n*k + j is local. Returns
     (C float64 [N, k, H] with zeros in unwritten slots, written bool [N, k])."""
-    C = np.zeros((N * k, H), dtype=np.float64)
+    C = np.zeros((N * k, H), dtype=Y.dtype)
     written = layout.pair_row >= 0
     rows = layout.pair_row[written]
     C[written] = w.reshape(-1)[written][:, None] * Y[rows]
@@ -218,7 +218,7 @@ def local_reduce(C: np.ndarray, written: np.ndarray) -> np.ndarray:
     """Source-side aggregation of this GPU's contributions: y[n] is the sum of
     the written slots of token n over ascending j."""
     N, k, H = C.shape
-    y = np.zeros((N, H), dtype=np.float64)
+    y = np.zeros((N, H), dtype=C.dtype)
     for j in range(k):
         y += np.where(written[:, j:j + 1], C[:, j, :], 0.0)
     return y
@@ -257,26 +257,30 @@ def decode_expert(inp, e: int):
     return bf16_bits_to_f64(inp.w1[e]), bf16_bits_to_f64(inp.w2[e])
 
 
-def run(inp, block_m: int = 128, idx=None, w=None, experts: int | None = None) -> OracleResult:
+def run(inp, block_m: int = 128, idx=None, w=None, experts: int | None = None,
+        float_type=np.float64) -> OracleResult:
     """The whole path: routing (unless idx/w are given), layout, per-expert
     FFN over the routed rows of each local expert, weighted combine and the
     source-side reduction. ``experts`` evaluates only the first that many
-    local experts (a bounded sample for timing; other rows stay zero)."""
+    local experts (a bounded sample for timing; other rows stay zero).
+    ``float_type`` is the type of the FFN and combine arithmetic: float64 for
+    parity; float32 only to time the plain fp32 CPU baseline (the same code in
+    single precision)."""
     wl = inp.wl
     N, k, H = wl.num_tokens, wl.top_k, wl.hidden
     if idx is None:
         idx, w = route(inp.logits, inp.bias, k)
     lay = dispatch_layout(idx, wl.local_begin, wl.num_local, block_m)
-    x = decode_x(inp)
-    Y = np.zeros((lay.total_rows, H), dtype=np.float64)
+    x = decode_x(inp).astype(float_type, copy=False)
+    Y = np.zeros((lay.total_rows, H), dtype=float_type)
     for e in range(wl.num_local if experts is None else min(experts, wl.num_local)):
         r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
         if r1 == r0:
             continue
         tokens = lay.row_pair[r0:r1] // k
-        W1, W2 = decode_expert(inp, e)
+        W1, W2 = (a.astype(float_type, copy=False) for a in decode_expert(inp, e))
         Y[r0:r1] = expert_ffn(x[tokens], W1, W2)
-    C, written = combine(np.asarray(w, np.float64), lay, Y, N, k, H)
+    C, written = combine(np.asarray(w, float_type), lay, Y, N, k, H)
     return OracleResult(idx, np.asarray(w, np.float64), lay, Y, C, written,
                         local_reduce(C, written))
 

@@ -429,9 +429,10 @@ def test_h_handoff_across_calls_with_poisoned_workspace(tile):
 
 TOL_FP8 = 5e-2
 # W4A8 (MX): h is requantised to e4m3 with power-of-two scales per 32 columns;
-# modelled on the CPU for the shapes below, that rounding alone moves the
-# per-row Linear-2 output by up to 6.0% of the row's largest value (the fp8
-# path's fp32-scaled h: 4.7%, inside its 5e-2 bar), so the bar here is 8e-2
+# the CPU model of that rounding (tests/test_tolerance_model.py, on the same
+# shapes and seeds) moves the per-row Linear-2 output by up to 6.0% of the
+# row's largest value (the fp8 path's fp32-scaled h: 4.7%, inside its 5e-2
+# bar), so the bar here is 8e-2
 TOL_W4A8 = 8e-2
 
 
@@ -514,9 +515,9 @@ def full_inputs(request):
 def test_full_size_sampled_rows(full_inputs, schedule):
     # every workload at full size in the launch configuration bench.py uses
     # (automatic plan), checked on sampled combine rows that the oracle
-    # evaluates one by one: the first, the last and two random rows of every
-    # local expert; a sample of non-local slots keeps the sentinel and no
-    # routed slot does
+    # evaluates one by one: the first and the last routed row of every
+    # scheduler row (M-block) and two random rows of every local expert; a
+    # sample of non-local slots keeps the sentinel and no routed slot does
     wl, inp = full_inputs
     up = Uploaded(inp)
     ffn = make_ffn(wl)
@@ -529,16 +530,22 @@ def test_full_size_sampled_rows(full_inputs, schedule):
     w = ffn.layout_bufs.topk_w.cpu().numpy().astype(np.float64)
     idx_ref, w_ref = mo.route(inp.logits, inp.bias, wl.top_k)
     assert (idx == idx_ref).all() and np.abs(w - w_ref).max() <= 1e-6
-    lay = mo.dispatch_layout(idx_ref, wl.local_begin, wl.num_local, ffn.plan.block_m)
+    bm = ffn.plan.block_m
+    lay = mo.dispatch_layout(idx_ref, wl.local_begin, wl.num_local, bm)
     rng = np.random.default_rng(11)
-    pairs = []
+    rows = set()
     for e in range(wl.num_local):
         r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
         if r1 > r0:
-            pairs += [int(lay.row_pair[r]) for r in sorted({r0, r1 - 1, *rng.integers(r0, r1, 2)})]
+            for b0 in range(r0, r1, bm):   # every M-block of the expert
+                rows |= {b0, min(b0 + bm, r1) - 1}
+            rows |= set(int(r) for r in rng.integers(r0, r1, 2))
+    pairs = [int(lay.row_pair[r]) for r in sorted(rows)]
     want = mo.row_outputs(inp, idx_ref, w_ref, pairs)
     err = row_rel_err(up.combine_rows_f64(pairs), want)
     tol = {"bf16": TOL_BF16, "fp8": TOL_FP8, "w4a8": TOL_W4A8}[wl.dtype]
+    print(f"[ffn] full-size {wl.name} {schedule}: {len(pairs)} rows over {int(lay.tile_offset[-1])} "
+          f"M-blocks, max per-row rel err {err.max():.4e} (bar {tol:.0e})", flush=True)
     assert err.max() <= tol, f"max per-row rel err {err.max():.3e}"
     nonlocal_ = np.nonzero(lay.pair_row < 0)[0]
     if len(nonlocal_):
@@ -547,6 +554,101 @@ def test_full_size_sampled_rows(full_inputs, schedule):
     routed = up.combine_rows_bits(lay.row_pair[rng.choice(len(lay.row_pair), min(2048, len(lay.row_pair)),
                                                           replace=False)])
     assert not (routed == 0xFFFF).any()
+
+
+def test_full_size_whole_expert_schedules_and_y_local(full_inputs):
+    # at full size: (1) the two schedules write bitwise-identical combine
+    # buffers; (2) every row of the expert with the most rows (the skewed
+    # workload's hottest expert spans ~64 M-blocks) against the oracle, in
+    # batches; (3) the combine audit is clean and y_local matches the oracle's
+    # per-token sum over local slots (ascending j) on sampled tokens
+    wl, inp = full_inputs
+    up = Uploaded(inp)
+    ffn = make_ffn(wl)
+    tol = {"bf16": TOL_BF16, "fp8": TOL_FP8, "w4a8": TOL_W4A8}[wl.dtype]
+    print(f"[ffn] full-size whole expert {wl.name} tile={ffn.plan.tile} grid={ffn.plan.grid}", flush=True)
+    _route_and_layout(ffn, up)
+    run_forward(ffn, up, schedule="expert_wave")
+    wave_bits = up.comb_all.clone()
+    up.reset_combine()
+    run_forward(ffn, up, schedule="interleaved")
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    assert torch.equal(wave_bits, up.comb_all), "schedules differ at full size"
+    del wave_bits
+    idx_ref, w_ref = mo.route(inp.logits, inp.bias, wl.top_k)
+    lay = mo.dispatch_layout(idx_ref, wl.local_begin, wl.num_local, ffn.plan.block_m)
+    counts = np.diff(lay.row_offset)
+    e = int(np.argmax(counts))
+    r0, r1 = int(lay.row_offset[e]), int(lay.row_offset[e + 1])
+    worst = 0.0
+    for b0 in range(r0, r1, 2048):
+        pairs = [int(f) for f in lay.row_pair[b0:min(b0 + 2048, r1)]]
+        err = row_rel_err(up.combine_rows_f64(pairs), mo.row_outputs(inp, idx_ref, w_ref, pairs))
+        worst = max(worst, float(err.max()))
+    print(f"[ffn] full-size {wl.name}: expert {e}, all {r1 - r0} rows "
+          f"({-(-(r1 - r0) // ffn.plan.block_m)} M-blocks), max per-row rel err {worst:.4e}", flush=True)
+    assert worst <= tol
+    # combine audit and y_local on sampled tokens
+    y = torch.empty((wl.num_tokens, wl.hidden), dtype=torch.float32, device=dev())
+    report = torch.zeros(4, dtype=torch.int32, device=dev())
+    ffn.combine_check(up.comb_slices, y=y, report=report)
+    torch.cuda.synchronize()
+    assert report.cpu().tolist() == [0, 0, 0, 0]
+    local = (lay.pair_row >= 0).reshape(wl.num_tokens, wl.top_k)
+    rng = np.random.default_rng(12)
+    has = np.nonzero(local.any(axis=1))[0]
+    toks = np.sort(rng.choice(has, min(48, len(has)), replace=False))
+    pairs = [int(n) * wl.top_k + j for n in toks for j in range(wl.top_k) if local[n, j]]
+    rows = mo.row_outputs(inp, idx_ref, w_ref, pairs)
+    ref_y = np.zeros((len(toks), wl.hidden))
+    pos = {int(n): i for i, n in enumerate(toks)}
+    for f, r in zip(pairs, rows):   # ascending j within each token
+        ref_y[pos[f // wl.top_k]] += r
+    got = y[torch.as_tensor(toks, device=dev())].cpu().numpy().astype(np.float64)
+    yerr = row_rel_err(got, ref_y)
+    print(f"[ffn] full-size {wl.name}: y_local on {len(toks)} tokens, max per-row rel err "
+          f"{yerr.max():.4e}", flush=True)
+    assert yerr.max() <= tol
+    none = np.nonzero(~local.any(axis=1))[0]
+    if len(none):
+        z = y[torch.as_tensor(none[:64], device=dev())]
+        assert (z == 0).all()
+
+
+@pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
+def test_large_tile_many_blocks_with_xcd_grouping_complete(schedule):
+    # the launch configuration of the skewed workload at a size the oracle
+    # finishes in seconds: the 256-row, eight-wavefront tile, experts of many
+    # M-blocks (Zipf-skewed routing), N1 = 2I/256 = 8 Linear-1 N-tiles, which
+    # divide the grid, so logical ids are grouped by N-tile per XCD; every
+    # local slot against the oracle, placement checked from the task trace
+    wl = _small_wl(num_slices=8, tokens_per_slice=256, num_experts=32, top_k=8, num_local=8, hidden=1024,
+                   inter=1024, skew=True, seed=1313)
+    inp = mi.make_inputs(wl)
+    ref = mo.run(inp, block_m=256)
+    counts = ref.layout.counts
+    assert counts.max() > 4 * 256 and (counts > 256).sum() >= 4
+    up = Uploaded(inp)
+    ffn = make_ffn(wl, tile=7)
+    plan = ffn.plan
+    assert plan.block_m == 256 and plan.n1_tiles == 8 and plan.grid % 8 == 0
+    cap = 256
+    trace = torch.full((plan.grid, cap, _lib.TRACE_WORDS), -1, dtype=torch.int32, device=dev())
+    print(f"[ffn] tile 7 many blocks {schedule}: counts {counts.tolist()} grid={plan.grid}", flush=True)
+    _route_and_layout(ffn, up)
+    run_forward(ffn, up, schedule=schedule, trace=trace, trace_capacity=cap)
+    torch.cuda.synchronize()
+    assert int(ffn.status.item()) == 0
+    _check_against_oracle(up, ref)
+    tr = trace.cpu().numpy()
+    want = sc.all_streams(schedule, plan.grid, ref.layout.tile_offset.tolist(), plan.n1_tiles, plan.n2_tiles,
+                          plan.lead_d, 0)
+    for g in range(plan.grid):
+        used = tr[g][tr[g][:, 0] != -1]
+        assert [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used] == want[g]
+        if len(used):   # grouped by N-tile: XCD x runs the ids with g mod 8 == x
+            assert g % 8 == int(used[0, 9]) % 8
 
 
 def test_wrapper_rejects_mismatched_buffers_before_launch():

@@ -395,3 +395,17 @@ def test_w4a8_oracle_uses_dequantized_inputs():
     pairs = np.nonzero(r.layout.pair_row >= 0)[0]
     got = mo.row_outputs(inp, r.idx, r.w, pairs)
     np.testing.assert_allclose(got, r.C.reshape(-1, 256)[pairs], rtol=0, atol=1e-13 * np.abs(C).max())
+
+
+def test_float32_setting_is_the_same_computation_in_single_precision():
+    # the CPU baseline times run(float_type=float32); it must be the float64
+    # definition up to single-precision rounding (the layout is shared)
+    wl = mi.get_workload("tiny")
+    inp = mi.make_inputs(wl)
+    a = mo.run(inp, block_m=16)
+    b = mo.run(inp, block_m=16, float_type=np.float32)
+    assert b.C.dtype == np.float32 and b.y_local.dtype == np.float32
+    assert (a.layout.row_pair == b.layout.row_pair).all()
+    err = np.abs(b.C - a.C).max(axis=2) / np.maximum(np.abs(a.C).max(axis=2), 1e-30)
+    assert err[a.written].max() < 1e-5
+    assert (b.C[~a.written] == 0).all()
