@@ -165,7 +165,9 @@ def main():
     ap.add_argument("--schedule", default="interleaved", choices=["interleaved", "expert_wave", "auto"],
                     help="auto: the schedule planner's recommendation for the workload's routing, "
                          "resolved once before the timed region")
-    ap.add_argument("--pairs", type=int, default=10, help="A-B-B-A rounds of the schedule comparison")
+    ap.add_argument("--pairs", type=int, default=10,
+                    help="A-B-B-A rounds of the schedule comparison (0: none, e.g. under a profiler, so that "
+                         "only the headline schedule is launched)")
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--tokens-per-slice", type=int, default=0,
                     help="run the workload's shapes at another batch size (workload name gets @T<n>)")
@@ -293,10 +295,11 @@ def main():
         sched_out[s_] = {"ffn_us_median": round(med * 1e3, 2), "ffn_us_min": round(min(v) * 1e3, 2),
                          "tflops": round(flops / (med * 1e-3) / 1e12, 2),
                          "hbm_gbs": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
-    speedup = (statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
-               if per["interleaved"] else None)
-    best_wave = min(statistics.median(per["expert_wave"]), statistics.median(per["expert_wave_one_wave"]))
-    speedup_best = best_wave / statistics.median(per["interleaved"])
+    speedup = speedup_best = None
+    if args.pairs > 0:
+        speedup = statistics.median(per["expert_wave"]) / statistics.median(per["interleaved"])
+        best_wave = min(statistics.median(per["expert_wave"]), statistics.median(per["expert_wave_one_wave"]))
+        speedup_best = best_wave / statistics.median(per["interleaved"])
     sclk = trace_clock(ffn, lambda **kw: ffn_call(dict(head_cfg, **kw)), ffn.plan.wall_clock_khz)
 
     if args.copy_calibration:
@@ -364,7 +367,7 @@ def main():
         "ffn_ms_p50_p90": [round(float(np.percentile(ffn_ms, 50)), 4), round(float(np.percentile(ffn_ms, 90)), 4)],
         "per_schedule": sched_out,
         "speedup_interleaved_over_wave": None if speedup is None else round(speedup, 4),
-        "speedup_interleaved_over_best_wave": round(speedup_best, 4),
+        "speedup_interleaved_over_best_wave": None if speedup_best is None else round(speedup_best, 4),
         "sclk_mhz_mainloop": sclk,
         "rocm": rocm_version(),
         "torch": torch.__version__,
@@ -378,7 +381,7 @@ def main():
                                                      / max(pred["given"]["makespan"], 1e-9), 4),
             "measured_wave_over_interleaved": None if speedup is None else round(speedup, 4),
             "recommended_is": same_as,
-            "measured_recommended_over_interleaved": round(
+            "measured_recommended_over_interleaved": None if args.pairs <= 0 else round(
                 statistics.median(per[same_as or "recommended"]) / statistics.median(per["interleaved"]), 4),
         },
         "roofline": roof,
