@@ -46,6 +46,9 @@ extern "C" {
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
 #define MOE_TRACE_WORDS 10      /* uint32 words per task record */
+/* Workspace held by the library for moe_ffn_forward_noalloc, per GPU. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+#define MOE_NOALLOC_MAX_SCHED_ROWS 16384
 
 typedef enum {
   MOE_OK = 0,
@@ -218,6 +221,30 @@ int32_t moe_ffn_forward(const moe_shape* shape, const moe_layout* layout,
                         void* const* combine_slices,
                         void* workspace, size_t workspace_bytes,
                         const moe_sched_params* params, void* stream);
+
+/* moe_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, kernels, outputs and
+ * status word as moe_ffn_forward, bit for bit; the workspace (h, its scales
+ * and the per-row counters) is a library-held device array of
+ * MOE_NOALLOC_WORKSPACE_BYTES on each GPU, held until the process ends.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call. The
+ * first call on a device clears the array's counters with a fill kernel on
+ * `stream`; every launch leaves them cleared again.
+ * Returns MOE_ERR_WORKSPACE_TOO_SMALL (before anything is enqueued) when the
+ * plan for the shape needs more than MOE_NOALLOC_MAX_SCHED_ROWS scheduler
+ * rows or more than the array holds (decode-sized batches fit: e.g. 128
+ * tokens in each of 8 slices of a DeepSeek-V3-shaped share of 32 experts,
+ * top-8 of 256, H = 7168, I = 2048).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from several threads without ordering)
+ * race and give wrong results; calls ordered on one stream are safe. */
+int32_t moe_ffn_forward_noalloc(const moe_shape* shape, const moe_layout* layout,
+                                const void* const* x_slices, const void* const* x_scales,
+                                const void* w1, const void* w1_scales,
+                                const void* w2, const void* w2_scales,
+                                void* const* combine_slices,
+                                const moe_sched_params* params, void* stream);
 
 /* Combine audit and source-side reduction (the "aggregate the top-k
  * results" half of Combine, X-Stage paper, section 2.2).

@@ -268,6 +268,23 @@ class MoeExpertFFN:
                          [t.data_ptr() for t in combine_slices], self.workspace.data_ptr(),
                          self.plan.workspace_bytes, params, _stream(stream))
 
+    def forward_noalloc(self, x_slices, w1, w2, combine_slices, x_scales=None, w1_scales=None,
+                        w2_scales=None, stream=None, **sched):
+        """forward() through moe_ffn_forward_noalloc: the workspace is the
+        library's own per-GPU array instead of this instance's, so the call
+        allocates nothing (shapes up to the array's size; larger ones raise
+        MoeError with MOE_ERR_WORKSPACE_TOO_SMALL). Calls that overlap on one
+        GPU share that array and race."""
+        if self.num_tokens:
+            self._check_buffers(x_slices, w1, w2, combine_slices, x_scales, w1_scales, w2_scales)
+        params = self.params(**sched)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        _lib.ffn_forward_noalloc(self.shape, self.layout_bufs.c_struct(),
+                                 [t.data_ptr() for t in x_slices],
+                                 None if x_scales is None else [t.data_ptr() for t in x_scales],
+                                 w1.data_ptr(), ptr(w1_scales), w2.data_ptr(), ptr(w2_scales),
+                                 [t.data_ptr() for t in combine_slices], params, _stream(stream))
+
     def combine_check(self, combine_slices, y=None, report=None, stream=None):
         """Source-side reduction of the local slots into ``y`` (fp32 [N, H])
         and, with ``report`` (int32 [4]), the sentinel audit; report[3]

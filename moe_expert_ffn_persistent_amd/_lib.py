@@ -26,7 +26,9 @@ MOE_MAX_SLICES = 64
 # every symbol include/moe_ffn.h declares
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_scratch_bytes", "moe_ffn_plan",
            "moe_workspace_init", "moe_dispatch_layout", "moe_ffn_forward", "moe_combine_check",
-           "moe_store_burst_probe", "moe_predict_schedule")
+           "moe_store_burst_probe", "moe_predict_schedule", "moe_ffn_forward_noalloc")
+NOALLOC_WORKSPACE_BYTES = 64 << 20
+NOALLOC_MAX_SCHED_ROWS = 16384
 
 c_i32 = ctypes.c_int32
 c_vp = ctypes.c_void_p
@@ -113,6 +115,9 @@ def load(path: str | None = None):
     lib.moe_ffn_forward.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), P(c_vp), c_vp, c_vp,
                                     c_vp, c_vp, P(c_vp), c_vp, ctypes.c_size_t,
                                     P(MoeSchedParams), c_vp]
+    lib.moe_ffn_forward_noalloc.restype = c_i32
+    lib.moe_ffn_forward_noalloc.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), P(c_vp), c_vp, c_vp,
+                                            c_vp, c_vp, P(c_vp), P(MoeSchedParams), c_vp]
     lib.moe_combine_check.restype = c_i32
     lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp, c_vp]
     lib.moe_store_burst_probe.restype = c_i32
@@ -170,6 +175,13 @@ def ffn_forward(shape, layout, x_ptrs, xs_ptrs, w1, w1s, w2, w2s, comb_ptrs, ws,
     check(load().moe_ffn_forward(ctypes.byref(shape), ctypes.byref(layout), ptr_array(x_ptrs),
                                  xs, w1, w1s, w2, w2s, ptr_array(comb_ptrs), ws, ws_bytes,
                                  ctypes.byref(params), stream), "moe_ffn_forward")
+
+
+def ffn_forward_noalloc(shape, layout, x_ptrs, xs_ptrs, w1, w1s, w2, w2s, comb_ptrs, params, stream):
+    xs = ptr_array(xs_ptrs) if xs_ptrs is not None else None
+    check(load().moe_ffn_forward_noalloc(ctypes.byref(shape), ctypes.byref(layout), ptr_array(x_ptrs),
+                                         xs, w1, w1s, w2, w2s, ptr_array(comb_ptrs),
+                                         ctypes.byref(params), stream), "moe_ffn_forward_noalloc")
 
 
 def combine_check(shape, layout, comb_ptrs, y_ptr, status_ptr, report_ptr, stream):

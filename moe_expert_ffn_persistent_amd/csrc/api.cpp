@@ -152,6 +152,25 @@ WsLayout carve(const moe_shape* s, int block_m, int max_rows) {
   return w;
 }
 
+// Workspace of the allocation-free entry point (moe_ffn_forward_noalloc):
+// the row counters and the done counter sit at fixed offsets, so that these
+// bytes only ever hold counters, which every launch leaves cleared, whatever
+// the shape of the call before; h and its scales follow.
+WsLayout carve_static(const moe_shape* s, int block_m, int max_rows) {
+  WsLayout w{};
+  const size_t rows = (size_t)max_rows * block_m;
+  const size_t elt = s->dtype == MOE_BF16 ? 2 : 1;
+  w.l2_full = 0;
+  w.done = (size_t)MOE_NOALLOC_MAX_SCHED_ROWS * 4;
+  w.h = align_up(w.done + 256, 256);
+  size_t off = align_up(w.h + rows * s->inter * elt, 256);
+  w.hs = off;
+  if (s->dtype == MOE_FP8_E4M3) off = align_up(off + rows * (s->inter / 128) * 4, 256);
+  if (s->dtype == MOE_W4A8) off = align_up(off + rows * (s->inter / 32), 256);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 bool shape_valid(const moe_shape* s) { return shape_ok(s); }
@@ -159,6 +178,132 @@ bool shape_valid(const moe_shape* s) { return shape_ok(s); }
 }  // namespace moe
 
 using namespace moe;
+
+// The allocation-free entry point's workspace: one copy per GPU, held from
+// the load of this library's code object until the process ends. In host
+// code this name is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device (static_workspace below).
+static __device__ __align__(256) char scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+struct StaticWorkspace {
+  bool ready = false;
+  char* ptr = nullptr;
+};
+StaticWorkspace g_static_ws[64];
+
+// Device address of `scratch` on the current device. On the first call on a
+// device its counter region is cleared by a fill kernel on `stream` (no
+// memset node, so a call under graph capture records a kernel).
+int static_workspace(char** out, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  StaticWorkspace& w = g_static_ws[dev];
+  if (!w.ready) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    if (launch_zero(p, (size_t)MOE_NOALLOC_MAX_SCHED_ROWS * 4 + 256, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    w.ptr = static_cast<char*>(p);
+    w.ready = true;
+  }
+  *out = w.ptr;
+  return MOE_OK;
+}
+
+// moe_ffn_forward and moe_ffn_forward_noalloc: argument checks, the
+// workspace carve (given workspace, or the fixed layout in `scratch`) and
+// the launch.
+int32_t ffn_forward_impl(const moe_shape* s, const moe_layout* lay, const void* const* x_slices,
+                         const void* const* x_scales, const void* w1, const void* w1_scales,
+                         const void* w2, const void* w2_scales, void* const* comb, void* ws,
+                         size_t ws_bytes, bool static_ws, const moe_sched_params* prm, void* stream) {
+  if (!shape_ok(s) || !lay || !prm || !x_slices || !comb || !w1 || !w2 || (!static_ws && !ws))
+    return MOE_ERR_INVALID_ARG;
+  const bool scaled = s->dtype != MOE_BF16;   // fp8 and W4A8 carry block scales
+  if (scaled && (!x_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  moe_plan plan{};
+  int st = moe_ffn_plan(s, prm, &plan);
+  if (st != MOE_OK) return st;
+  if (lay->block_m != plan.block_m) return MOE_ERR_INVALID_ARG;
+  const WsLayout w = static_ws ? carve_static(s, plan.block_m, plan.max_sched_rows)
+                               : carve(s, plan.block_m, plan.max_sched_rows);
+  if (static_ws) {
+    if (plan.max_sched_rows > MOE_NOALLOC_MAX_SCHED_ROWS || w.total > MOE_NOALLOC_WORKSPACE_BYTES)
+      return MOE_ERR_WORKSPACE_TOO_SMALL;
+  } else if (ws_bytes < plan.workspace_bytes) {
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (!lay->row_offset || !lay->tile_offset || !lay->row_pair || !lay->row_weight)
+    return MOE_ERR_INVALID_ARG;
+  if (prm->trace && prm->trace_capacity < 1) return MOE_ERR_INVALID_ARG;
+  if (num_tokens(s) == 0) return MOE_OK;
+  for (int i = 0; i < s->num_slices; ++i)
+    if (!x_slices[i] || !comb[i] || (scaled && !x_scales[i])) return MOE_ERR_INVALID_ARG;
+  DeviceProps* dp = nullptr;
+  st = device_props(&dp);
+  if (st != MOE_OK) return st;
+  if (static_ws) {
+    char* p = nullptr;
+    st = static_workspace(&p, (hipStream_t)stream);
+    if (st != MOE_OK) return st;
+    ws = p;
+  }
+
+  FfnArgs a{};
+  a.S = s->num_slices;
+  a.T = s->tokens_per_slice;
+  a.k = s->top_k;
+  a.L = s->num_local_experts;
+  a.H = s->hidden;
+  a.I = s->inter;
+  a.N1 = plan.n1_tiles;
+  a.N2 = plan.n2_tiles;
+  a.grid = plan.grid;
+  // Group logical ids by Linear-1 N-tile per XCD when the experts span
+  // several M-blocks (their weight tiles are then read once per XCD instead
+  // of once per M-block); otherwise keep a row's N-tiles on one XCD.
+  {
+    const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
+    const bool fits = a.grid % 8 == 0 && a.N1 % 8 == 0 && a.grid % a.N1 == 0;
+    const bool want = MOE_XCD_BY_NTILE > 0 || (MOE_XCD_BY_NTILE < 0 && avg >= 2.0 * plan.block_m);
+    a.xcd_group = fits && want ? a.N1 / 8 : 0;
+  }
+  a.schedule = prm->schedule;
+  a.lead_d = plan.lead_d;
+  a.experts_per_wave = prm->experts_per_wave;
+  a.debug_skip_row = prm->debug_skip_l1_row;
+  a.trace_cap = prm->trace ? prm->trace_capacity : 0;
+  a.timeout_ticks = (long long)(prm->timeout_ms > 0 ? prm->timeout_ms : 2000) * dp->wall_khz;
+  for (int i = 0; i < s->num_slices; ++i) {
+    a.x[i] = x_slices[i];
+    a.xs[i] = x_scales ? static_cast<const float*>(x_scales[i]) : nullptr;
+    a.comb[i] = comb[i];
+  }
+  a.w1 = w1;
+  a.w1s = static_cast<const float*>(w1_scales);
+  a.w2 = w2;
+  a.w2s = static_cast<const float*>(w2_scales);
+  a.row_offset = lay->row_offset;
+  a.tile_offset = lay->tile_offset;
+  a.row_pair = lay->row_pair;
+  a.row_weight = lay->row_weight;
+  char* base = static_cast<char*>(ws);
+  a.h = base + w.h;
+  a.hs = reinterpret_cast<float*>(base + w.hs);
+  a.l2_full = reinterpret_cast<int32_t*>(base + w.l2_full);
+  a.done = reinterpret_cast<int32_t*>(base + w.done);
+  a.status = prm->status;
+  a.trace = prm->trace;
+  const hipError_t err = s->dtype == MOE_FP8_E4M3 ? launch_ffn_fp8(plan.tile, a, (hipStream_t)stream)
+                         : s->dtype == MOE_W4A8   ? launch_ffn_w4a8(plan.tile, a, (hipStream_t)stream)
+                                                  : launch_ffn_bf16(plan.tile, a, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -298,79 +443,21 @@ int32_t moe_dispatch_layout(const moe_shape* s, const float* logits, const float
   return launch_layout(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+
 int32_t moe_ffn_forward(const moe_shape* s, const moe_layout* lay, const void* const* x_slices,
                         const void* const* x_scales, const void* w1, const void* w1_scales,
                         const void* w2, const void* w2_scales, void* const* comb, void* ws,
                         size_t ws_bytes, const moe_sched_params* prm, void* stream) {
-  if (!shape_ok(s) || !lay || !prm || !x_slices || !comb || !w1 || !w2 || !ws)
-    return MOE_ERR_INVALID_ARG;
-  const bool scaled = s->dtype != MOE_BF16;   // fp8 and W4A8 carry block scales
-  if (scaled && (!x_scales || !w1_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
-  moe_plan plan{};
-  int st = moe_ffn_plan(s, prm, &plan);
-  if (st != MOE_OK) return st;
-  if (lay->block_m != plan.block_m) return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < plan.workspace_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!lay->row_offset || !lay->tile_offset || !lay->row_pair || !lay->row_weight)
-    return MOE_ERR_INVALID_ARG;
-  if (prm->trace && prm->trace_capacity < 1) return MOE_ERR_INVALID_ARG;
-  if (num_tokens(s) == 0) return MOE_OK;
-  for (int i = 0; i < s->num_slices; ++i)
-    if (!x_slices[i] || !comb[i] || (scaled && !x_scales[i])) return MOE_ERR_INVALID_ARG;
-  DeviceProps* dp = nullptr;
-  st = device_props(&dp);
-  if (st != MOE_OK) return st;
+  return ffn_forward_impl(s, lay, x_slices, x_scales, w1, w1_scales, w2, w2_scales, comb, ws, ws_bytes,
+                          false, prm, stream);
+}
 
-  const WsLayout w = carve(s, plan.block_m, plan.max_sched_rows);
-  FfnArgs a{};
-  a.S = s->num_slices;
-  a.T = s->tokens_per_slice;
-  a.k = s->top_k;
-  a.L = s->num_local_experts;
-  a.H = s->hidden;
-  a.I = s->inter;
-  a.N1 = plan.n1_tiles;
-  a.N2 = plan.n2_tiles;
-  a.grid = plan.grid;
-  // Group logical ids by Linear-1 N-tile per XCD when the experts span
-  // several M-blocks (their weight tiles are then read once per XCD instead
-  // of once per M-block); otherwise keep a row's N-tiles on one XCD.
-  {
-    const double avg = (double)num_tokens(s) * s->top_k / s->num_experts;
-    const bool fits = a.grid % 8 == 0 && a.N1 % 8 == 0 && a.grid % a.N1 == 0;
-    const bool want = MOE_XCD_BY_NTILE > 0 || (MOE_XCD_BY_NTILE < 0 && avg >= 2.0 * plan.block_m);
-    a.xcd_group = fits && want ? a.N1 / 8 : 0;
-  }
-  a.schedule = prm->schedule;
-  a.lead_d = plan.lead_d;
-  a.experts_per_wave = prm->experts_per_wave;
-  a.debug_skip_row = prm->debug_skip_l1_row;
-  a.trace_cap = prm->trace ? prm->trace_capacity : 0;
-  a.timeout_ticks = (long long)(prm->timeout_ms > 0 ? prm->timeout_ms : 2000) * dp->wall_khz;
-  for (int i = 0; i < s->num_slices; ++i) {
-    a.x[i] = x_slices[i];
-    a.xs[i] = x_scales ? static_cast<const float*>(x_scales[i]) : nullptr;
-    a.comb[i] = comb[i];
-  }
-  a.w1 = w1;
-  a.w1s = static_cast<const float*>(w1_scales);
-  a.w2 = w2;
-  a.w2s = static_cast<const float*>(w2_scales);
-  a.row_offset = lay->row_offset;
-  a.tile_offset = lay->tile_offset;
-  a.row_pair = lay->row_pair;
-  a.row_weight = lay->row_weight;
-  char* base = static_cast<char*>(ws);
-  a.h = base + w.h;
-  a.hs = reinterpret_cast<float*>(base + w.hs);
-  a.l2_full = reinterpret_cast<int32_t*>(base + w.l2_full);
-  a.done = reinterpret_cast<int32_t*>(base + w.done);
-  a.status = prm->status;
-  a.trace = prm->trace;
-  const hipError_t err = s->dtype == MOE_FP8_E4M3 ? launch_ffn_fp8(plan.tile, a, (hipStream_t)stream)
-                         : s->dtype == MOE_W4A8   ? launch_ffn_w4a8(plan.tile, a, (hipStream_t)stream)
-                                                  : launch_ffn_bf16(plan.tile, a, (hipStream_t)stream);
-  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+int32_t moe_ffn_forward_noalloc(const moe_shape* s, const moe_layout* lay, const void* const* x_slices,
+                                const void* const* x_scales, const void* w1, const void* w1_scales,
+                                const void* w2, const void* w2_scales, void* const* comb,
+                                const moe_sched_params* prm, void* stream) {
+  return ffn_forward_impl(s, lay, x_slices, x_scales, w1, w1_scales, w2, w2_scales, comb, nullptr, 0, true,
+                          prm, stream);
 }
 
 int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, float* y,
