@@ -161,7 +161,7 @@ struct Tile {
   // they overlap.
   // Only the first NTB token blocks are multiplied (the others hold padding
   // rows only); the copies are spread over the MFMAs that remain.
-  template <bool COH, int NTB>
+  template <bool COH, int NTB, bool COPY = true>
   __device__ __forceinline__ void compute(const char* stage, int wf, int wt, size_t off, uint32_t slot) {
     constexpr int KS = C::BK / 16;
     constexpr int NMF = C::FB * NTB;     // MFMAs per k-step
@@ -185,7 +185,7 @@ struct Tile {
         }
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
-          if (C::issue_slot(i, KS * NMF) == ks * NMF + m) issue_one<COH>(i, off, slot);
+          if (COPY && C::issue_slot(i, KS * NMF) == ks * NMF + m) issue_one<COH>(i, off, slot);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -194,11 +194,13 @@ struct Tile {
   // Full K loop over nk stages of BK through an NS-stage LDS ring. Stage kt
   // is awaited (own copies, then one workgroup barrier, after which every
   // wavefront is also done with stage kt-1), then multiplied while the copy of
-  // stage kt+NS-1 goes into the slot stage kt-1 used. The copy is issued
-  // unconditionally (the last NS-1 stages re-copy stage nk-1 into their free
-  // slot), so no branch splits the MFMA sequence it is spread over; those
-  // extra copies are awaited at the end, before the epilogue reuses LDS.
-  // acc starts at zero; token blocks NTB and up stay zero.
+  // stage kt+NS-1 goes into the slot stage kt-1 used. The last NS-1 stages
+  // have no later stage to copy and run a stage body without copies (chosen
+  // outside the unrolled MFMA sequence, which no branch splits), so the
+  // epilogue starts without waiting on a copy nobody reads. With fewer stages
+  // than the ring holds, the prologue repeats the last stage into the spare
+  // slots; those copies are older than the last stage's wait, which awaits
+  // them all. acc starts at zero; token blocks NTB and up stay zero.
   template <bool COH, int NTB = C::TB>
   __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
 #pragma unroll
@@ -213,16 +215,21 @@ struct Tile {
       for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, off, ring + s * C::STAGE_BYTES);
     }
     int slot = 0;
-    for (int kt = 0; kt < nk; ++kt) {
+    const int nmain = nk - (C::NS - 1);   // stages that copy a later stage
+    for (int kt = 0; kt < nmain; ++kt) {
       vm_wait<C::NI * (C::NS - 2)>();   // stage kt has landed (later stages may not have)
       lds_barrier();
-      const int nxt = min(kt + C::NS - 1, nk - 1);
       const int nslot = slot == 0 ? C::NS - 1 : slot - 1;
-      compute<COH, NTB>(lds + slot * C::STAGE_BYTES, wf, wt, (size_t)nxt * C::ROW_BYTES,
+      compute<COH, NTB>(lds + slot * C::STAGE_BYTES, wf, wt, (size_t)(kt + C::NS - 1) * C::ROW_BYTES,
                         ring + nslot * C::STAGE_BYTES);
       slot = slot + 1 == C::NS ? 0 : slot + 1;
     }
-    vm_wait<0>();
+    for (int kt = max(nmain, 0); kt < nk; ++kt) {
+      vm_wait_ahead<C::NI, C::NS - 2>(nk - 1 - kt);   // copies of the later stages may be in flight
+      lds_barrier();
+      compute<COH, NTB, false>(lds + slot * C::STAGE_BYTES, wf, wt, 0, 0);
+      slot = slot + 1 == C::NS ? 0 : slot + 1;
+    }
   }
 };
 
@@ -264,7 +271,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
   // XCDs, so consecutive logical ids are placed on the same XCD (and share
   // its L2) when the grid is a multiple of 8
   const int G = a.grid;
-  const int g = logical_instance(G, a.xcd_group);
+  const int g = logical_instance(G, a.xcd_group, a.xcd_bx);
 
   InterleavedStream ist;
   ExpertWaveStream ews;

@@ -53,15 +53,27 @@ enum CachePolicy { kCacheNormal = 0, kStream = 1, kCoherent = 2 };
 // Logical instance id of this workgroup. Workgroups are dispatched
 // round-robin over the 8 XCDs (block b runs on XCD b mod 8), each with its
 // own L2. By default consecutive logical ids share an XCD, so the N-tiles of
-// one row (which read the same token rows) meet in one L2. With xcd_group R,
-// XCD x holds the ids with g mod N1 in [xR, xR+R): when N1 divides the grid,
-// an instance's Linear-1 tiles all have N-tile g mod N1, so the M-blocks of
-// one expert that read the same weight tile meet in one L2.
-__device__ __forceinline__ int logical_instance(int G, int xcd_group) {
+// one row (which read the same token rows) meet in one L2.
+// With N-tile grouping (xcd_group = N1/8 > 0, N1 dividing G), instance g's
+// Linear-1 tiles all have N-tile g mod N1 and row slot g / N1 of each round
+// of G tiles. The round's grid of G/N1 row slots x N1 N-tiles is cut into
+// 8 blocks, xcd_bx blocks along the N-tiles and 8/xcd_bx along the row
+// slots, one per XCD: the M-blocks that read one weight tile and the N-tiles
+// that read one token block then meet in one L2, and an XCD fetches the
+// sum, not the product, of its block's sides. xcd_bx = 8 gives each XCD
+// N1/8 N-tiles across every row slot.
+__device__ __forceinline__ int logical_instance(int G, int xcd_group, int xcd_bx) {
   const int b = (int)blockIdx.x;
   if (G % 8 != 0) return b;
   const int x = b % 8, i = b / 8;
-  if (xcd_group > 0) return (i / xcd_group) * (8 * xcd_group) + x * xcd_group + i % xcd_group;
+  if (xcd_group > 0) {
+    const int N1 = 8 * xcd_group;
+    const int nw = N1 / xcd_bx;              // N-tiles per block
+    const int rh = (G / N1) / (8 / xcd_bx);  // row slots per block
+    const int r = (x / xcd_bx) * rh + i / nw;
+    const int n = (x % xcd_bx) * nw + i % nw;
+    return r * N1 + n;
+  }
   return x * (G / 8) + i;
 }
 

@@ -306,6 +306,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_w4a8(const FfnArgs a) {
   __shared__ int pair_s[C::TM];   // routed pair and router weight of each row of a
   __shared__ float wgt_s[C::TM];  // Linear-2 tile (fetch_rows)
   Meta& meta = metam.m;
+  // with L2-cached h loads: drop lines an earlier launch left in this XCD's L2
+  if (!MOE_H_COHERENT) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -326,7 +328,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_w4a8(const FfnArgs a) {
   __syncthreads();
   const int P = uni(meta.tile_off[L]);
   const int G = a.grid;
-  const int g = logical_instance(G, a.xcd_group);
+  const int g = logical_instance(G, a.xcd_group, a.xcd_bx);
 
   InterleavedStream ist;
   ExpertWaveStream ews;

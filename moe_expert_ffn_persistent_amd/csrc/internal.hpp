@@ -54,8 +54,9 @@ struct FfnArgs {
   int S, T, k, L, H, I;
   int N1, N2;              // Linear-1 / Linear-2 N-tiles per scheduler row
   int grid;                // persistent workgroups (== gridDim.x)
-  int xcd_group;           // logical-id placement: 0 = consecutive ids per XCD; R > 0 = the ids
-                           // with g mod N1 in [x*R, x*R+R) on XCD x (N1 == 8R, N1 | grid)
+  int xcd_group;           // logical-id placement: 0 = consecutive ids per XCD; R > 0 = grouped by
+                           // Linear-1 N-tile (N1 == 8R, N1 | grid): see logical_instance
+  int xcd_bx;              // with xcd_group: XCD blocks along the N-tiles (1, 2, 4 or 8)
   int schedule;            // moe_schedule
   int lead_d;              // Interleaved lead D (>= 1)
   int experts_per_wave;    // 0 = greedy

@@ -146,6 +146,21 @@ def test_task_trace_matches_schedule_model(schedule, grid, lead, epw):
         assert len(set(used[:, 9].tolist())) == 1
 
 
+XCD_BX = 4   # XCD blocks along the N-tiles (the library's default split)
+
+
+def _xcd_block(g, grid, n1, bx=XCD_BX):
+    """XCD that N-tile grouping places logical instance g on: the round's grid
+    of grid/n1 row slots x n1 N-tiles is cut into bx blocks along the N-tiles
+    and 8/bx along the row slots (every XCD N1/8 N-tiles across all row slots
+    when the sides do not divide)."""
+    rs = grid // n1
+    if n1 % bx or rs % (8 // bx):
+        bx = 8
+    r, n = g // n1, g % n1
+    return (r // (rs // (8 // bx))) * bx + n // (n1 // bx)
+
+
 @pytest.mark.parametrize("schedule", ["expert_wave", "interleaved"])
 def test_xcd_placement_by_ntile_changes_nothing_but_placement(schedule):
     # tile 3 (32 x 128) with I = 1024 gives N1 = 16 Linear-1 N-tiles and
@@ -185,7 +200,7 @@ def test_xcd_placement_by_ntile_changes_nothing_but_placement(schedule):
                 continue
             b = int(used[0, 9])
             if grid == 32:
-                assert (g % 16) // 2 == b % 8
+                assert _xcd_block(g, grid, 16) == b % 8
             else:
                 assert g == (b % 8) * (grid // 8) + b // 8
         bits[grid] = up.combine_bits().copy()
@@ -647,8 +662,8 @@ def test_large_tile_many_blocks_with_xcd_grouping_complete(schedule):
     for g in range(plan.grid):
         used = tr[g][tr[g][:, 0] != -1]
         assert [(int(r[0]) & 3, int(r[1]), int(r[0]) >> 2) for r in used] == want[g]
-        if len(used):   # grouped by N-tile: XCD x runs the ids with g mod 8 == x
-            assert g % 8 == int(used[0, 9]) % 8
+        if len(used):   # grouped by N-tile: one block of the round's grid per XCD
+            assert _xcd_block(g, plan.grid, plan.n1_tiles) == int(used[0, 9]) % 8
 
 
 def test_wrapper_rejects_mismatched_buffers_before_launch():
