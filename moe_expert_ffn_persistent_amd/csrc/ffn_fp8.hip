@@ -95,6 +95,22 @@ struct Cfg8 {
 
 constexpr int kMaxKBlocks = 128;   // H/128 and I/128 limit
 
+// Physical 16-byte chunk of logical chunk c in 128-byte row r of an operand
+// stage: c ^ ((r >> 1) & 7) ^ ((c & 2) << 1), a bijection of the row's 8
+// chunks (and its own inverse up to the row term). The fragment reads take
+// rows r16 = lane mod 16 at logical chunks 2g and 2g+1 for lane group
+// g = lane / 16. Measured on MI355X with rocprofv3's SQ_LDS_BANK_CONFLICT,
+// a 128-bit LDS read with the row term alone conflicts two ways (half of all
+// LDS cycles, 1.8x the read time), because the lanes served together are not
+// 16 consecutive ones; the (c & 2) << 1 term moves the odd lane groups to the
+// other half of the banks and makes both reads conflict-free.
+__device__ __forceinline__ int chunk_of(int r, int c) { return c ^ ((r >> 1) & 7) ^ ((c & 2) << 1); }
+// logical chunk held by physical chunk p of row r (the inverse)
+__device__ __forceinline__ int logical_chunk(int r, int p) {
+  const int q = p ^ ((r >> 1) & 7);
+  return q ^ ((q & 2) << 1);
+}
+
 // Operand and token-scale copies, shared by both fp8 tiles.
 template <class C>
 struct Tile8Copies {
@@ -110,7 +126,7 @@ struct Tile8Copies {
     for (int i = 0; i < C::NID; ++i) {
       const int j = wave + C::NW * i;
       const int r = j * C::RPI + lane / C::CPR;
-      const int c = (lane % C::CPR) ^ ((r >> 1) & 7);   // see the bf16 kernel's swizzle
+      const int c = logical_chunk(r, lane % C::CPR);   // lands at physical chunk lane % 8
       const char* base = j * C::RPI < C::TN ? wrow(r) : trow(r - C::TN);
       src[i] = base + c * 16;
     }
@@ -155,10 +171,9 @@ struct Tile8Copies {
   // token row's swizzle is the same whether counted from the weight rows or
   // from its own stage)
   __device__ __forceinline__ static i32x8 frag32(const char* stage, int r, int c) {
-    const int swz = (r >> 1) & 7;
     const char* row = stage + r * C::ROW_BYTES;
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + ((c ^ swz) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((c + 1) ^ swz) << 4));
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (chunk_of(r, c) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (chunk_of(r, c + 1) << 4));
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 
