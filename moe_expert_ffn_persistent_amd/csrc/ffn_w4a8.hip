@@ -57,6 +57,19 @@ struct CfgMx {
   static_assert(SP >= 1 && SP <= 8, "spread in eighths of the stage");
 };
 
+// Physical 16-byte chunk of logical chunk q (the K quarter lane group q
+// reads) in 64-byte weight row r: q ^ ((r >> 2) & 3) ^ ((q & 1) << 1), a
+// bijection of the row's 4 chunks. The row term alone spreads 16 rows of one
+// chunk over all banks, but measured on MI355X (rocprofv3
+// SQ_LDS_BANK_CONFLICT, an LDS probe of this read) the 128-bit reads of the
+// four lane groups still conflict two ways; the (q & 1) << 1 term removes it.
+__device__ __forceinline__ int wchunk_of(int r, int q) { return q ^ ((r >> 2) & 3) ^ ((q & 1) << 1); }
+// logical chunk held by physical chunk p of weight row r (the inverse)
+__device__ __forceinline__ int wlogical_chunk(int r, int p) {
+  const int x = p ^ ((r >> 2) & 3);
+  return x ^ ((x & 1) << 1);
+}
+
 template <class C>
 struct TileMx {
   const char* asrc[C::NIA];   // this lane's weight-row chunk, stage 0
@@ -66,7 +79,7 @@ struct TileMx {
   f32x4 acc[C::FB16][C::TB16];
 
   // Weight copy i of wavefront w fills rows [16j, 16j+16), j = w + NW*i, lane
-  // l row 16j + l/4, physical chunk l%4 (logical chunk l%4 ^ ((row>>2)&3));
+  // l row 16j + l/4, physical chunk l%4 (logical chunk wlogical_chunk(row, l%4));
   // token copy i fills rows [8j, 8j+8), lane l row 8j + l/8, physical chunk
   // l%8 (logical l%8 ^ ((row>>1)&7)). Scale word q = 64w + lane: weight row
   // q, token row q - TN (rows past TN + TM repeat the last token row).
@@ -77,7 +90,7 @@ struct TileMx {
 #pragma unroll
     for (int i = 0; i < C::NIA; ++i) {
       const int r = (wave + C::NW * i) * 16 + lane / 4;
-      asrc[i] = arow(r) + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+      asrc[i] = arow(r) + (wlogical_chunk(r, lane & 3) << 4);   // lands at physical chunk lane % 4
     }
 #pragma unroll
     for (int i = 0; i < C::NIB; ++i) {
@@ -129,7 +142,7 @@ struct TileMx {
     int sa[C::FB16], sb[2];
     auto afrag = [&](int i) {
       const int r = wf * C::FT + i * 16 + r16;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * C::A_ROW + ((q ^ ((r >> 2) & 3)) << 4));
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * C::A_ROW + (wchunk_of(r, q) << 4));
       af[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       sa[i] = (int)(sw[r] >> (8 * q));
     };
