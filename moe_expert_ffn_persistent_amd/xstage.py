@@ -291,8 +291,19 @@ def tile_spans(trace: np.ndarray, khz: int) -> dict:
     # Linear-2 store spans in flight alongside each one, itself included
     k_act = burst_concurrency(np.round(a * khz / 1e3), np.round(b * khz / 1e3))
     pct = lambda x, q: float(np.percentile(x, q)) if len(x) else float("nan")
+    # natural gap of each workgroup between its Linear-2 bursts: from one
+    # tile's stores issued to the next Linear-2 tile's mainloop end (the
+    # work that separates two bursts of one producer, section 3.2's G)
+    gaps = []
+    for g in range(trace.shape[0]):
+        t = tr[g][tr[g][:, 0] != 0xFFFFFFFF]
+        t = t[(t[:, 0] & 3) == 2]
+        if len(t) > 1:
+            gaps.append(_wrap(t[1:, 4] - t[:-1, 5]) * us)
+    gaps = np.concatenate(gaps) if gaps else np.zeros(0)
     return {
         "l2_tiles": int(l2.sum()),
+        "l2_gap_us": {"median": pct(gaps, 50), "p10": pct(gaps, 10)},
         "t_rs_us": {"median": pct(t_rs, 50), "p90": pct(t_rs, 90), "max": pct(t_rs, 100)},
         "drain_lag_us": {"median": pct(lag, 50), "p90": pct(lag, 90)},
         "k_act": {"median": pct(k_act, 50), "p90": pct(k_act, 90)},
@@ -368,11 +379,50 @@ def model_checks(cal: dict, spans: dict) -> dict:
     return checks
 
 
+def stall_table(pr: "Prober", cal: dict, spans: dict, bursts: int = 8) -> dict:
+    """Table 2 of the X-Stage paper for this GPU: per schedule, the Linear-2
+    stall per tile that the store model predicts against the one the trace
+    measures. The model's burst is one tile's combine rows (block_m rows of
+    block_n bf16 values each) from K_act producers at once (the measured
+    number of Linear-2 store spans in flight), separated by the measured
+    natural gap G of a producer's Linear-2 bursts. Its backpressure-free
+    issue time T_iss0 is the L2-resident control of the probe at exactly that
+    K, B, row size and gap; Eq. 3 gives T_RS = max(T_iss0, V/R - G) with
+    V = K_act B, and Eq. 15 the stall, max(0, T_RS - T_cover) with
+    T_cover = 0 (the workgroup that computes a tile issues its stores before
+    its next task). The probe's scattered run at the same K, B and G is the
+    store path alone; the trace's T_RS adds the epilogue's own work (router
+    weight, bf16 conversion, LDS staging)."""
+    R = cal["R_bytes_per_us"]
+    B = spans["combine_bytes_per_tile"]
+    row = spans["block_n"] * 2
+    out = {}
+    for sched in ("expert_wave", "interleaved"):
+        s = spans.get(sched)
+        if not s:
+            continue
+        K = max(1, int(round(s["k_act"]["median"])))
+        G = max(0.0, s["l2_gap_us"]["median"])
+        ctl = pr.run(K, B, G, bursts=bursts, control=True, row_bytes=row)
+        sca = pr.run(K, B, G, bursts=bursts, control=False, row_bytes=row)
+        t0 = ctl.steady()[0]
+        V = K * B
+        pred = float(t_iss(G, V, t0, R))
+        out[sched] = {"K_act": K, "B_bytes": B, "gap_us": G, "V_bytes": V, "V_over_R_us": V / R,
+                      "t_iss0_us": t0, "backpressure_us": float(delta_t_iss(G, V, t0, R)),
+                      "pred_t_rs_us": pred, "pred_stall_us": float(critical_stall(pred, 0.0)),
+                      "probe_t_iss_us": sca.steady()[0],
+                      "meas_stall_us": s["t_rs_us"]["median"], "meas_stall_p90_us": s["t_rs_us"]["p90"],
+                      "epilogue_work_us": s["t_rs_us"]["median"] - sca.steady()[0]}
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="dsv3", help="comma-separated workload names")
     ap.add_argument("--producers", type=int, default=256)
     ap.add_argument("--spans-only", action="store_true", help="skip the probe calibration")
+    ap.add_argument("--calibration", help="reuse the calibration of an earlier run's JSON output")
     args = ap.parse_args(argv)
     if args.spans_only:
         out = {"workloads": {}}
@@ -382,12 +432,16 @@ def main(argv=None):
         print(json.dumps(out, default=float), flush=True)
         return 0
     pr = Prober()
-    cal = calibrate(pr, K=args.producers)
-    del pr
+    if args.calibration:
+        cal = json.loads(open(args.calibration).read().strip().splitlines()[-1])["calibration"]
+    else:
+        cal = calibrate(pr, K=args.producers)
+    print("[xstage] calibration done", file=sys.stderr, flush=True)
     out = {"calibration": cal, "workloads": {}}
     for name in args.workload.split(","):
         spans = ffn_spans(name)
-        out["workloads"][name] = {"spans": spans, "model_checks": model_checks(cal, spans)}
+        out["workloads"][name] = {"spans": spans, "model_checks": model_checks(cal, spans),
+                                  "stall_table": stall_table(pr, cal, spans)}
         print(f"[xstage] {name} done", file=sys.stderr, flush=True)
     print(json.dumps(out, default=float), flush=True)
 
