@@ -377,6 +377,10 @@ def main():
                                 "interleaved": round(pred["given"]["makespan"], 1),
                                 "recommended": round(rec["makespan"], 1),
                                 "lower_bound": round(pred["lower_bound"], 1)},
+            "predicted_hbm_gb": {"expert_wave": round(pred["candidates"][0]["hbm_bytes"] / 1e9, 3),
+                                 "interleaved": round(pred["given"]["hbm_bytes"] / 1e9, 3),
+                                 "recommended": round(rec["hbm_bytes"] / 1e9, 3),
+                                 "compulsory": round(pred["given"]["unique_bytes"] / 1e9, 3)},
             "predicted_wave_over_interleaved": round(pred["candidates"][0]["makespan"]
                                                      / max(pred["given"]["makespan"], 1e-9), 4),
             "measured_wave_over_interleaved": None if speedup is None else round(speedup, 4),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 2
+#define MOE_FFN_ABI_VERSION 3
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
 #define MOE_TRACE_WORDS 10      /* uint32 words per task record */
@@ -277,7 +277,13 @@ typedef struct {
   double makespan;           /* predicted kernel time in model units (see below)         */
   double working_set;        /* time-averaged bytes of the expert weight matrices (an
                                 expert's W1 or W2) that running tasks read              */
+  double hbm_bytes;          /* predicted reads that miss an LRU cache of
+                                MOE_PLANNER_CACHE_BYTES (the Infinity Cache): weight
+                                tiles and activation blocks, in the model's start order */
+  double unique_bytes;       /* bytes of those reads read at least once (compulsory)     */
 } moe_schedule_estimate;
+
+#define MOE_PLANNER_CACHE_BYTES (256.0 * 1024 * 1024)
 
 #define MOE_MAX_SCHEDULE_CANDIDATES 8
 
@@ -316,10 +322,19 @@ typedef struct {
  * Interleaved with D = knee, Expert-Wave with all local experts in one wave,
  * Interleaved with D = knee/2, 2 knee, 4 knee and P, each capped at P (a
  * lead of P or more behaves as P; duplicates dropped).
+ * Locality: the reads of the tasks, in the model's start order (time, then
+ * instance), go through an LRU cache of MOE_PLANNER_CACHE_BYTES, an entry
+ * being what a task reads whole: its weight tile (the N-tile's rows of the
+ * expert's W1 or W2) and its activation block (the M-block's token rows for
+ * Linear-1, its h rows for Linear-2). Misses are hbm_bytes.
  * Recommendation, among the candidates predicted within 2% of the fastest:
  * the first of the two first candidates (the original order, then the knee
- * lead), else the one with the smallest working set (the earlier one on a
- * tie).
+ * lead), else the first of them; replaced by the one with the fewest
+ * hbm_bytes (the earlier one on a tie) when that is lower by more than 2% of
+ * the chosen one's unique_bytes. (The X-Stage paper, section 6.3, weighs
+ * stall against weight locality; on this GPU the locality that orders lose
+ * is the Infinity Cache's, when many experts of a few M-blocks each run at
+ * once.)
  * Returns MOE_ERR_INVALID_ARG for a NULL pointer, a negative count, counts
  * whose M-blocks exceed plan->max_sched_rows or plan fields that are not
  * positive. */

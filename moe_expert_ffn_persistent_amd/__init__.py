@@ -26,7 +26,7 @@ SCHEDULE_NAMES = {v: k for k, v in SCHEDULES.items()}
 def _estimate(e) -> dict:
     return {"schedule": SCHEDULE_NAMES[e.schedule], "lead_d": e.lead_d,
             "experts_per_wave": e.experts_per_wave, "makespan": e.makespan,
-            "working_set": e.working_set}
+            "working_set": e.working_set, "hbm_bytes": e.hbm_bytes, "unique_bytes": e.unique_bytes}
 
 
 def prediction_dict(pred) -> dict:

@@ -64,7 +64,11 @@ MAX_SCHEDULE_CANDIDATES = 8
 
 class MoeScheduleEstimate(ctypes.Structure):
     _fields_ = [("schedule", c_i32), ("lead_d", c_i32), ("experts_per_wave", c_i32),
-                ("makespan", ctypes.c_double), ("working_set", ctypes.c_double)]
+                ("makespan", ctypes.c_double), ("working_set", ctypes.c_double),
+                ("hbm_bytes", ctypes.c_double), ("unique_bytes", ctypes.c_double)]
+
+
+PLANNER_CACHE_BYTES = 256.0 * 1024 * 1024
 
 
 class MoeSchedulePrediction(ctypes.Structure):
