@@ -4,7 +4,8 @@ A step is one pass of the whole path over one batch of synthetic input:
 routing + dispatch layout (moe_dispatch_layout), the persistent fused FFN
 (moe_ffn_forward: Linear-1 + SwiGLU, Linear-2 + weighted combine stores) and
 the source-side reduction of the combine slots (moe_combine_check with
-y_local). Inputs are resident in HBM before the timed region starts.
+y_local, in bf16 by default: the model's activation format). Inputs are
+resident in HBM before the timed region starts.
 
 Prints one JSON line. ``value`` is TFLOP/s of the algorithmic FLOPs
 (6*H*I per routed row) over the whole step, for the schedule named in
@@ -172,6 +173,8 @@ def main():
     ap.add_argument("--tokens-per-slice", type=int, default=0,
                     help="run the workload's shapes at another batch size (workload name gets @T<n>)")
     ap.add_argument("--lead-d", type=int, default=0)
+    ap.add_argument("--y-dtype", default="bf16", choices=["bf16", "fp32"],
+                    help="element type of the reduced output y_local")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -207,7 +210,8 @@ def main():
     w1s = None if inp.w1_scale is None else up(inp.w1_scale)
     w2s = None if inp.w2_scale is None else up(inp.w2_scale)
     comb = torch.empty((S, T, k, H), dtype=torch.int16, device=dev)
-    y = torch.empty((wl.num_tokens, H), dtype=torch.float32, device=dev)
+    y = torch.empty((wl.num_tokens, H), dtype=torch.bfloat16 if args.y_dtype == "bf16" else torch.float32,
+                    device=dev)
     x_sl = [x[s] for s in range(S)]
     xs_sl = None if xs is None else [xs[s] for s in range(S)]
     c_sl = [comb[s] for s in range(S)]
@@ -356,7 +360,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded normal inputs, random-init expert weights)",
         "config": {"workload": wl.name, "schedule": args.schedule, "schedule_config": head_cfg, "slices": S,
-                   "tokens_per_slice": T, "experts": wl.num_experts, "top_k": k,
+                   "tokens_per_slice": T, "experts": wl.num_experts, "top_k": k, "y_dtype": args.y_dtype,
                    "local_experts": wl.num_local, "hidden": H, "inter": wl.inter,
                    "routed_rows": R, "sched_rows": P, "max_rows_per_expert": max_rows,
                    "active_experts": active, "tile": plan.tile, "block_m": plan.block_m,

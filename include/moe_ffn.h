@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 3
+#define MOE_FFN_ABI_VERSION 4
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
 #define MOE_TRACE_WORDS 10      /* uint32 words per task record */
@@ -246,11 +246,19 @@ int32_t moe_ffn_forward_noalloc(const moe_shape* shape, const moe_layout* layout
                                 void* const* combine_slices,
                                 const moe_sched_params* params, void* stream);
 
+/* Element type of moe_combine_check's y_local. */
+#define MOE_Y_FP32 0
+#define MOE_Y_BF16 1
+
 /* Combine audit and source-side reduction (the "aggregate the top-k
  * results" half of Combine, X-Stage paper, section 2.2).
  *   combine_slices host array [S] of device pointers, each [T, k, H] bf16.
- *   y_local        [N, H] fp32 or NULL: y_local[n] = sum over the local
- *                  slots j of token n, in ascending j, of combine[n, j].
+ *   y_local        [N, H] or NULL: y_local[n] = sum over the local slots j
+ *                  of token n, in ascending j, of combine[n, j], summed in
+ *                  fp32 and stored as y_dtype says.
+ *   y_dtype        MOE_Y_FP32 (the fp32 sum) or MOE_Y_BF16 (that sum rounded
+ *                  to nearest even bf16: the model's activation format, half
+ *                  the bytes written).
  *   status         device int32 or NULL: the status word the FFN calls
  *                  wrote (moe_sched_params.status), read on the stream after
  *                  them.
@@ -266,7 +274,7 @@ int32_t moe_ffn_forward_noalloc(const moe_shape* shape, const moe_layout* layout
  *                  The audit reads every slot; pass NULL to skip it.
  * Neither the status word nor the report is cleared by the library. */
 int32_t moe_combine_check(const moe_shape* shape, const moe_layout* layout,
-                          void* const* combine_slices, float* y_local,
+                          void* const* combine_slices, void* y_local, int32_t y_dtype,
                           const int32_t* status, int32_t* report, void* stream);
 
 /* One schedule configuration and what the planner's model predicts for it. */

@@ -90,7 +90,8 @@ def check_layout_inputs(shape: MoeShape, logits=None, bias=None, topk_idx=None, 
 
 def check_combine_inputs(shape: MoeShape, combine_slices, y=None, report=None, device_type="cuda"):
     """Buffers of moe_combine_check: S combine slices of [T, k, H] 2-byte
-    (bf16) elements, an optional fp32 y_local [N, H] and int32 report [4]."""
+    (bf16) elements, an optional fp32 or bf16 y_local [N, H] and int32
+    report [4]."""
     S, T, k, H = shape.num_slices, shape.tokens_per_slice, shape.top_k, shape.hidden
     if len(combine_slices) != S:
         raise ValueError(f"need {S} combine slices, got {len(combine_slices)}")
@@ -99,7 +100,9 @@ def check_combine_inputs(shape: MoeShape, combine_slices, y=None, report=None, d
             raise ValueError("combine slices hold 2-byte (bf16) elements")
         _need(t, "combine slice", T * k * H * 2, None, device_type)
     if y is not None:
-        _need(y, "y_local", S * T * H * 4, torch.float32, device_type)
+        if y.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"y_local must be float32 or bfloat16, got {y.dtype}")
+        _need(y, "y_local", S * T * H * y.element_size(), y.dtype, device_type)
     if report is not None:
         _need(report, "report", 16, torch.int32, device_type)
 
@@ -286,13 +289,16 @@ class MoeExpertFFN:
                                  [t.data_ptr() for t in combine_slices], params, _stream(stream))
 
     def combine_check(self, combine_slices, y=None, report=None, stream=None):
-        """Source-side reduction of the local slots into ``y`` (fp32 [N, H])
-        and, with ``report`` (int32 [4]), the sentinel audit; report[3]
-        receives this instance's device status word."""
+        """Source-side reduction of the local slots into ``y`` ([N, H]; the
+        fp32 sum, or that sum rounded to bf16 when ``y`` is bfloat16) and,
+        with ``report`` (int32 [4]), the sentinel audit; report[3] receives
+        this instance's device status word."""
         check_combine_inputs(self.shape, combine_slices, y, report, self.device.type)
         _lib.combine_check(self.shape, self.layout_bufs.c_struct(),
                            [t.data_ptr() for t in combine_slices],
-                           None if y is None else y.data_ptr(), self.status.data_ptr(),
+                           None if y is None else y.data_ptr(),
+                           _lib.MOE_Y_BF16 if y is not None and y.dtype == torch.bfloat16 else _lib.MOE_Y_FP32,
+                           self.status.data_ptr(),
                            None if report is None else report.data_ptr(), _stream(stream))
 
     def check_status(self, clear: bool = True) -> None:

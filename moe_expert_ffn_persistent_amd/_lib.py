@@ -22,6 +22,8 @@ MOE_W4A8 = 2
 MOE_SCHED_EXPERT_WAVE = 0
 MOE_SCHED_INTERLEAVED = 1
 MOE_MAX_SLICES = 64
+MOE_Y_FP32 = 0
+MOE_Y_BF16 = 1
 
 # every symbol include/moe_ffn.h declares
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_scratch_bytes", "moe_ffn_plan",
@@ -123,7 +125,7 @@ def load(path: str | None = None):
     lib.moe_ffn_forward_noalloc.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), P(c_vp), c_vp, c_vp,
                                             c_vp, c_vp, P(c_vp), P(MoeSchedParams), c_vp]
     lib.moe_combine_check.restype = c_i32
-    lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_vp, c_vp, c_vp]
+    lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_i32, c_vp, c_vp, c_vp]
     lib.moe_store_burst_probe.restype = c_i32
     lib.moe_store_burst_probe.argtypes = [P(MoeBurstParams), c_vp, ctypes.c_size_t, c_vp, c_vp]
     lib.moe_predict_schedule.restype = c_i32
@@ -188,9 +190,9 @@ def ffn_forward_noalloc(shape, layout, x_ptrs, xs_ptrs, w1, w1s, w2, w2s, comb_p
                                          ctypes.byref(params), stream), "moe_ffn_forward_noalloc")
 
 
-def combine_check(shape, layout, comb_ptrs, y_ptr, status_ptr, report_ptr, stream):
+def combine_check(shape, layout, comb_ptrs, y_ptr, y_dtype, status_ptr, report_ptr, stream):
     check(load().moe_combine_check(ctypes.byref(shape), ctypes.byref(layout),
-                                   ptr_array(comb_ptrs), y_ptr, status_ptr, report_ptr, stream),
+                                   ptr_array(comb_ptrs), y_ptr, y_dtype, status_ptr, report_ptr, stream),
           "moe_combine_check")
 
 

@@ -474,9 +474,10 @@ int32_t moe_ffn_forward_noalloc(const moe_shape* s, const moe_layout* lay, const
                           prm, stream);
 }
 
-int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, float* y,
-                          const int32_t* status, int32_t* report, void* stream) {
+int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const* comb, void* y,
+                          int32_t y_dtype, const int32_t* status, int32_t* report, void* stream) {
   if (!shape_ok(s) || !lay || !lay->pair_row || !comb) return MOE_ERR_INVALID_ARG;
+  if (y_dtype != MOE_Y_FP32 && y_dtype != MOE_Y_BF16) return MOE_ERR_INVALID_ARG;
   CheckArgs a{};
   a.S = s->num_slices;
   a.T = s->tokens_per_slice;
@@ -489,6 +490,7 @@ int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const
   }
   a.pair_row = lay->pair_row;
   a.y = y;
+  a.y_bf16 = y_dtype == MOE_Y_BF16;
   a.status = status;
   a.report = report;
   return launch_check(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -4,7 +4,7 @@
 // (token, top-k slot); the X-Stage paper's Combine then aggregates the top-k
 // results of each token (section 2.2). This kernel does that aggregation for
 // the slots this GPU owns (y_local[n] = sum over local j, ascending j, in
-// fp32) and, optionally, audits the buffers against the 0xFFFF sentinel the
+// fp32, stored as fp32 or rounded to bf16) and, optionally, audits the buffers against the 0xFFFF sentinel the
 // caller filled them with: every local slot must have been written, and no
 // other slot may have been touched.
 //
@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
   const uint32_t visit = audit ? (uint32_t)((1ull << a.k) - 1ull) : local_mask;
   uint32_t unwritten = 0, clobbered = 0, nonfinite = 0;
   const char* __restrict__ base = static_cast<const char*>(a.comb[s]) + (size_t)t * a.k * a.H * 2;
-  float* __restrict__ yrow = a.y ? a.y + (size_t)n * a.H : nullptr;
+  char* __restrict__ yrow = a.y ? static_cast<char*>(a.y) + (size_t)n * a.H * (a.y_bf16 ? 2 : 4) : nullptr;
   const int nquad = a.H / 4;
   for (int q0 = 0; q0 < nquad; q0 += kQuads * kThreads) {
     float y[kQuads][4];
@@ -85,12 +85,21 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
     }
     if (yrow) {   // streamed out: not re-read here
       typedef float f32x4 __attribute__((ext_vector_type(4)));
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int u = 0; u < kQuads; ++u) {
         const int q = q0 + u * kThreads + (int)threadIdx.x;
-        if (q < nquad)
+        if (q >= nquad) continue;
+        if (a.y_bf16) {
+          // the hardware conversion rounds to nearest even
+          const bf16x2 lo = {(__bf16)y[u][0], (__bf16)y[u][1]}, hi = {(__bf16)y[u][2], (__bf16)y[u][3]};
+          __builtin_nontemporal_store(u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)},
+                                      reinterpret_cast<u32x2*>(yrow + (size_t)q * 8));
+        } else {
           __builtin_nontemporal_store(f32x4{y[u][0], y[u][1], y[u][2], y[u][3]},
-                                      reinterpret_cast<f32x4*>(yrow + q * 4));
+                                      reinterpret_cast<f32x4*>(yrow + (size_t)q * 16));
+        }
       }
     }
   }

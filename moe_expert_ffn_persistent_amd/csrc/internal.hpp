@@ -97,7 +97,8 @@ struct CheckArgs {
   int S, T, k, H, L;
   void* comb[MOE_MAX_SLICES];
   const int32_t* pair_row;
-  float* y;
+  void* y;
+  int y_bf16;              // y is bf16 (round to nearest even) instead of fp32
   const int32_t* status;   // FFN status word or nullptr (copied to report[3])
   int32_t* report;
 };

@@ -76,10 +76,12 @@ def test_combine_inputs_accept_the_right_buffers():
     check_combine_inputs(shape(), comb(), f32(N, H), i32(4), device_type="cpu")
     check_combine_inputs(shape(), [torch.zeros(T, K, H, dtype=torch.bfloat16) for _ in range(S)],
                          device_type="cpu")
+    check_combine_inputs(shape(), comb(), torch.zeros(N, H, dtype=torch.bfloat16), device_type="cpu")
 
 
 @pytest.mark.parametrize("case", ["slices_count", "slice_dtype", "slice_short", "slice_noncontig",
-                                  "y_dtype", "y_short", "report_short", "report_dtype"])
+                                  "y_dtype", "y_half", "y_short", "y_bf16_short", "report_short",
+                                  "report_dtype"])
 def test_combine_inputs_reject_mismatches(case):
     c, y, rep = comb(), f32(N, H), i32(4)
     if case == "slices_count":
@@ -92,8 +94,12 @@ def test_combine_inputs_reject_mismatches(case):
         c[0] = torch.zeros(H, K, T, dtype=torch.int16).permute(2, 1, 0)
     elif case == "y_dtype":
         y = torch.zeros(N, H, dtype=torch.float64)[:, : H // 2]
+    elif case == "y_half":
+        y = torch.zeros(N, H, dtype=torch.float16)
     elif case == "y_short":
         y = f32(N, H - 1)
+    elif case == "y_bf16_short":
+        y = torch.zeros(N, H - 1, dtype=torch.bfloat16)
     elif case == "report_short":
         rep = i32(3)
     elif case == "report_dtype":

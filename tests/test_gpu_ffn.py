@@ -298,6 +298,16 @@ def test_combine_check_two_passes_and_every_audit_flag():
     has = ref.written.any(axis=1)
     assert has.any() and (~ref.written).any()
     assert row_rel_err(got.astype(np.float64), ref.y_local)[has].max() <= TOL_BF16
+    # bf16 output: that same fp32 sum rounded to nearest even, bit for bit
+    # (the rounding written out on the integer bits: add 0x7FFF plus the
+    # lowest kept bit, keep the high half; every value here is finite)
+    yb = torch.full((wl.num_tokens, wl.hidden), float("nan"), dtype=torch.bfloat16, device=dev())
+    ffn.combine_check(up.comb_slices, y=yb)
+    torch.cuda.synchronize()
+    u = want.view(np.uint32).astype(np.uint64)
+    want_b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    got_b = yb.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_b, want_b)
     # plant, all past the first pass: a non-local slot written, a local slot
     # with one element left at the sentinel, another local slot holding +inf
     S_T = wl.tokens_per_slice
