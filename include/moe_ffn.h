@@ -129,14 +129,17 @@ typedef struct {
                                 word 1 = scheduler row p,
                                 words 2..5 = low 32 bits of the device wall clock
                                 (moe_plan.wall_clock_khz) at task start, after the
-                                dependency wait, after the mainloop, and when every
-                                wavefront has issued its epilogue stores (Linear-2:
-                                the sender-visible end of the combine stores;
-                                Linear-1: the row counter was published),
+                                dependency wait, after the mainloop, and when the
+                                epilogue stores were issued (Linear-2: the
+                                sender-visible end of the combine stores),
                                 words 6..7 = low 32 bits of the shader clock counter
                                 at task start and after the mainloop,
                                 word 8 = wall clock when the epilogue stores have
-                                completed (Linear-2; equal to word 5 for Linear-1),
+                                completed (Linear-2) or the row counter was
+                                published (Linear-1: the bf16 kernel publishes
+                                during the workgroup's next task, the fp8 and W4A8
+                                kernels as soon as the h stores complete, with
+                                word 5 = word 8),
                                 word 9 = hardware workgroup id (blockIdx.x; it runs
                                 on XCD word9 mod 8).
                                 Unused records stay untouched                          */

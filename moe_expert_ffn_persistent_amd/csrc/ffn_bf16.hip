@@ -201,8 +201,9 @@ struct Tile {
   // than the ring holds, the prologue repeats the last stage into the spare
   // slots; those copies are older than the last stage's wait, which awaits
   // them all. acc starts at zero; token blocks NTB and up stay zero.
-  template <bool COH, int NTB = C::TB>
-  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt) {
+  // after_prologue runs once the prologue's copies are issued.
+  template <bool COH, int NTB = C::TB, class Hook>
+  __device__ __forceinline__ void mainloop(char* lds, int nk, int wf, int wt, Hook&& after_prologue) {
 #pragma unroll
     for (int fb = 0; fb < C::FB; ++fb)
 #pragma unroll
@@ -214,6 +215,7 @@ struct Tile {
 #pragma unroll
       for (int i = 0; i < C::NI; ++i) issue_one<COH>(i, off, ring + s * C::STAGE_BYTES);
     }
+    after_prologue();
     int slot = 0;
     const int nmain = nk - (C::NS - 1);   // stages that copy a later stage
     for (int kt = 0; kt < nmain; ++kt) {
@@ -281,6 +283,23 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 
   Tile<C> tile;
   tile.ring = (uint32_t)(uintptr_t)lds;
+  // A Linear-1 task's row counter is published during the next task: after
+  // a Linear-1 task's prologue copies are issued (the wait for the h stores
+  // then overlaps their latency), before a Linear-2 task's dependency wait
+  // (which may be on that very row), or after the last task. Publishing
+  // waits for every wavefront's h stores to complete, then increments the
+  // counter (row p_pub; seq_pub numbers that task's record).
+  int p_pub = -1, seq_pub = 0;
+  auto publish = [&]() {
+    if (p_pub >= 0) {
+      vm_wait<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p_pub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.trace && seq_pub < a.trace_cap && tid == 0)
+        a.trace[((size_t)g * a.trace_cap + seq_pub) * kTraceWords + 8] = (uint32_t)wall_clock64();
+      p_pub = -1;
+    }
+  };
   int seq = 0;
   for (;;) {
     const Task t = interleaved ? ist.next() : ews.next();
@@ -308,6 +327,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     if (l1) {
       if (p == a.debug_skip_row) continue;
     } else {
+      publish();
       // ---- wait until every Linear-1 tile of row p has published h ----
       if (tid == 0) {
         int ok = 1;
@@ -365,11 +385,11 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     // 101-128 rows in a 160-row block).
     const bool short_blk = C::WT == 1 && C::TB > 1 && Me - m * C::TM <= C::TM - 32;
     if (short_blk) {
-      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false, short_tb<C>()>(lds, nk, wf, wt);
-      else tile.template mainloop<true, short_tb<C>()>(lds, nk, wf, wt);
+      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false, short_tb<C>()>(lds, nk, wf, wt, publish);
+      else tile.template mainloop<true, short_tb<C>()>(lds, nk, wf, wt, publish);
     } else {
-      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt);
-      else tile.template mainloop<true>(lds, nk, wf, wt);
+      if (l1 || !MOE_H_COHERENT) tile.template mainloop<false>(lds, nk, wf, wt, publish);
+      else tile.template mainloop<true>(lds, nk, wf, wt, publish);
     }
     if (rec) {
       rec[4] = (uint32_t)wall_clock64();
@@ -412,12 +432,10 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
         // device scope: written through this XCD's L2 for the consuming XCD
         store16<kCoherent>(hb + (size_t)row * I * 2 + c * 16, v);
       }
-      // publish: every wavefront's h stores have completed before the row
-      // counter moves
-      vm_wait<0>();
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(a.l2_full + p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (rec) rec[5] = rec[8] = (uint32_t)wall_clock64();
+      // published during the next task (or after the last one)
+      p_pub = p;
+      seq_pub = seq - 1;
+      if (rec) rec[5] = (uint32_t)wall_clock64();
     } else {
       // weighted combine rows: bf16(w * acc), features n*TN .. n*TN + TN.
       // Destinations first (one row per thread, independent loads that
@@ -461,6 +479,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
     }
   }
 
+  publish();
   // ---- completion: the last workgroup to finish clears the counters ----
   __syncthreads();
   if (tid == 0) {

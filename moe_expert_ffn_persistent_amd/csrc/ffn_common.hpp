@@ -29,7 +29,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+// silu(g) = g * sigmoid(g) with the hardware reciprocal (v_rcp_f32, 1 ulp)
+// instead of a correctly rounded division: the division's scale/fixup
+// sequence was most of the Linear-1 epilogue's VALU work, and h is rounded
+// to bf16 or fp8 right after. For g -> -inf, exp(-g) overflows to inf and the
+// reciprocal gives 0, as the division does.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // Cache policy of a copy: kCacheNormal (weights and x rows; measured on
 // MI355X, non-temporal copies stream weights markedly slower), kStream (nt),
