@@ -17,7 +17,8 @@
 // consecutive hidden elements (an 8-byte load per slot, a 16-byte store), so
 // one load instruction of a wavefront covers 512 contiguous bytes of a slot
 // row and one store 1 KiB of the y row; a thread's loads of all its quads of
-// one slot are issued together, ahead of the arithmetic and of the stores.
+// one slot are issued together, and before the arithmetic of the slot
+// before it, so two slots' loads are in flight at a time.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -54,15 +55,22 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
     for (int u = 0; u < kQuads; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[u][i] = 0.f;
-    for (uint32_t m = visit; m; m &= m - 1) {
-      const int j = __builtin_ctz(m);
-      const bool local = (local_mask >> j) & 1;
-      uint2 v[kQuads];
+    // the loads of the next slot go out before this slot's arithmetic, so
+    // two slots' loads are in flight at a time
+    uint2 v[kQuads], vn[kQuads];
+    auto load_slot = [&](int j, uint2 (&dst)[kQuads]) {
 #pragma unroll
       for (int u = 0; u < kQuads; ++u) {
         const int q = q0 + u * kThreads + (int)threadIdx.x;
-        if (q < nquad) v[u] = *reinterpret_cast<const uint2*>(base + ((size_t)j * a.H + q * 4) * 2);
+        if (q < nquad) dst[u] = *reinterpret_cast<const uint2*>(base + ((size_t)j * a.H + q * 4) * 2);
       }
+    };
+    if (visit) load_slot(__builtin_ctz(visit), v);
+    for (uint32_t m = visit; m; m &= m - 1) {
+      const int j = __builtin_ctz(m);
+      const bool local = (local_mask >> j) & 1;
+      const uint32_t rest = m & (m - 1);
+      if (rest) load_slot(__builtin_ctz(rest), vn);
 #pragma unroll
       for (int u = 0; u < kQuads; ++u) {
         const int q = q0 + u * kThreads + (int)threadIdx.x;
@@ -82,6 +90,8 @@ __global__ void __launch_bounds__(kThreads) combine_check(CheckArgs a) {
           }
         }
       }
+#pragma unroll
+      for (int u = 0; u < kQuads; ++u) v[u] = vn[u];
     }
     if (yrow) {   // streamed out: not re-read here
       typedef float f32x4 __attribute__((ext_vector_type(4)));
