@@ -411,16 +411,20 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 #pragma unroll
         for (int fp = 0; fp < C::FB / 2; ++fp) {
           const int col0 = (wf * (C::FB / 2) + fp) * 32 + (lane_e >> 5) * 4;
+          // one gate/up block pair at a time (accumulators held in AGPRs are
+          // then read out block by block instead of all at once)
+          f32x16 gate = tile.acc[2 * fp][tb], up = tile.acc[2 * fp + 1][tb];
+          asm volatile("" : "+v"(gate), "+v"(up));
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             float hv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              hv[i] = silu(tile.acc[2 * fp][tb][g4 * 4 + i]) * tile.acc[2 * fp + 1][tb][g4 * 4 + i];
+            for (int i = 0; i < 4; ++i) hv[i] = silu(gate[g4 * 4 + i]) * up[g4 * 4 + i];
             const uint64_t v = (uint64_t)pack_bf16x2(hv[0], hv[1]) |
                                ((uint64_t)pack_bf16x2(hv[2], hv[3]) << 32);
             *reinterpret_cast<uint64_t*>(lds + stage_off<HROW>(tok_l, (col0 + g4 * 8) * 2)) = v;
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       __syncthreads();
@@ -457,13 +461,16 @@ __global__ void __launch_bounds__(C::THREADS, 1) moe_ffn_bf16(const FfnArgs a) {
 #pragma unroll
         for (int fb = 0; fb < C::FB; ++fb) {
           const int col0 = wf * C::FT + fb * 32 + (lane_e >> 5) * 4;
+          // one block at a time (see the Linear-1 epilogue)
+          f32x16 v = tile.acc[fb][tb];
+          asm volatile("" : "+v"(v));
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x16& v = tile.acc[fb][tb];
             const uint64_t o = (uint64_t)pack_bf16x2(w * v[g4 * 4 + 0], w * v[g4 * 4 + 1]) |
                                ((uint64_t)pack_bf16x2(w * v[g4 * 4 + 2], w * v[g4 * 4 + 3]) << 32);
             *reinterpret_cast<uint64_t*>(lds + stage_off<CROW>(tok_l, (col0 + g4 * 8) * 2)) = o;
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       __syncthreads();
