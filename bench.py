@@ -264,6 +264,31 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ffn.check_status()
 
+    # ---- the same step captured once in a HIP graph and replayed (after
+    # the timed region; the headline figures above are the eager step) ----
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(head_cfg)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(head_cfg)
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = round((time.perf_counter() - t1) * 1e3 / args.steps, 4)
+        del graph
+    except RuntimeError as err:   # reported, not fatal: the eager step is the measurement
+        graph_ms = f"capture failed: {err}"[:200]
+    ffn.check_status()
+
     # ---- paired schedule comparison, FFN only, A-B-C-C-B-A: both orders
     # with their default parameters, and the planner's recommendation ----
     arms = {"expert_wave": {"schedule": "expert_wave"}, "interleaved": {"schedule": "interleaved"},
@@ -369,6 +394,7 @@ def main():
                    "r_expert": round(max_rows / (wl.num_tokens * k / wl.num_experts), 3)},
         "pct_of_mfma_peak": round(100 * flops / (ms_per_step * 1e-3) / 1e12 / peak_flops, 2),
         "ffn_only_ms": round(statistics.mean(ffn_ms), 4),
+        "graph_ms_per_step": graph_ms,
         "ffn_ms_p50_p90": [round(float(np.percentile(ffn_ms, 50)), 4), round(float(np.percentile(ffn_ms, 90)), 4)],
         "per_schedule": sched_out,
         "speedup_interleaved_over_wave": None if speedup is None else round(speedup, 4),
