@@ -166,9 +166,12 @@ struct TileMx {
       // formats: A 4 = e2m1, B 0 = e4m3; scale bytes in bits 7..0 (op_sel 0)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j & 1], acc[i][j], 4, 0, 0, sa[i],
                                                                    0, sb[j & 1]);
+      // the scale-word and token-row copies of the stage go out before its
+      // weight-row copies: the gathered token rows come back later (measured
+      // on MI355X: 2.3% faster Interleaved, 3.3% Expert-Wave)
 #pragma unroll
       for (int k = 0; k < C::NI; ++k)
-        if (C::issue_slot(k) == b) issue_one<COH>(k, kt_next, slot);
+        if (C::issue_slot(k) == b) issue_one<COH>(C::NI - 1 - k, kt_next, slot);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
