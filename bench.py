@@ -108,9 +108,11 @@ def cpu_baseline(inp, seconds_budget: float):
         res = mo.run(inp, block_m=128, experts=n_exp, float_type=np.float32)
         dt = time.perf_counter() - t1
         rows = int(res.layout.row_offset[n_exp])
+        # the next sample (twice the experts; its time estimated from its
+        # routed rows) must end within the budget
+        next_rows = int(res.layout.row_offset[min(wl.num_local, 2 * n_exp)])
         del res
-        # the next sample (twice the experts) must end within the budget
-        if time.perf_counter() - t0 + 2.1 * dt > seconds_budget:
+        if n_exp < wl.num_local and time.perf_counter() - t0 + dt * max(1.0, next_rows / max(rows, 1)) > seconds_budget:
             break
     times = [dt]
     while n_exp == wl.num_local and time.perf_counter() - t0 + 1.2 * dt < seconds_budget:
