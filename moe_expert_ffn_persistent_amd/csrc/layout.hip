@@ -175,15 +175,17 @@ __global__ void __launch_bounds__(kWave) layout_count(LayoutArgs a) {
   for (int e = lane; e < a.L; e += kWave) a.block_counts[(size_t)blockIdx.x * a.L + e] = s_cnt[e];
 }
 
-constexpr int kScanLds = 8192;   // ints of block counts staged in LDS per pass
+// ints of block counts staged in LDS per pass: 128 KiB, so that the counts
+// of up to 992 chunks of 32 experts (253,952 pairs) take one pass
+constexpr int kScanLds = 32768;
 
 // Exclusive scan of every expert's column of block_counts over the chunks,
 // then the per-expert totals, row and tile offsets. The counts pass through
 // LDS in row batches (coalesced global traffic; rows padded to L+1 ints so a
 // column read hits distinct banks); one wavefront scans one column at a time.
 __global__ void __launch_bounds__(1024) layout_scan(LayoutArgs a) {
-  extern __shared__ int s_tot[];   // [L] running per-expert totals, then the staging rows
-  int* s_buf = s_tot + a.L;
+  extern __shared__ int s_tot[];   // [L] running per-expert totals
+  __shared__ int s_buf[kScanLds];   // staging rows
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
@@ -304,7 +306,7 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   }
   const size_t lds = sizeof(int) * (size_t)a.L;
   if (a.nchunks > 0) layout_count<<<a.nchunks, kWave, lds, stream>>>(a);
-  layout_scan<<<1, 1024, lds + sizeof(int) * kScanLds, stream>>>(a);
+  layout_scan<<<1, 1024, lds, stream>>>(a);
   if (a.nchunks > 0) layout_place<<<a.nchunks, kWave, lds, stream>>>(a);
   return hipGetLastError();
 }
