@@ -386,6 +386,32 @@ typedef struct {
 int32_t moe_store_burst_probe(const moe_burst_params* params, void* dst, size_t dst_bytes,
                               uint32_t* stamps, void* stream);
 
+/* MFMA issue-rate probe: the rate the matrix cores sustain when nothing but
+ * MFMAs runs, on every CU, under the board's power limit -- the ceiling
+ * beside the dense MFMA figures against which the FFN kernels' roofline
+ * fractions are read (the X-Stage paper's evaluation reads its kernels
+ * against the Tensor Core activity of its GPU, section 5.2.2).
+ *   format    0: v_mfma_f32_32x32x16_bf16 (32,768 FLOP per MFMA);
+ *             1: v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 x e4m3 (65,536);
+ *             2: v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 x e4m3 (131,072).
+ *   blocks    workgroups of MOE_MFMA_PROBE_THREADS threads (two wavefronts
+ *             per SIMD), 1..65535; one per CU fills the chip.
+ *   iters     loop trips, >= 1; each wavefront issues 16 MFMAs per trip.
+ *   operands  device buffer of MOE_MFMA_PROBE_OPERAND_BYTES random operand
+ *             bytes (bf16 values for format 0, e4m3 codes otherwise; each
+ *             wavefront loads 16 fragments once, from one of 64 slots).
+ *   stamps    device int64 [blocks][2]: shader-clock cycles (s_memtime) and
+ *             wall-clock ticks (moe_plan.wall_clock_khz) of each workgroup's
+ *             MFMA loop.
+ *   sink      device float [blocks * MOE_MFMA_PROBE_THREADS]: the
+ *             accumulator sums, written so that the loop is not removed.
+ * Enqueued on `stream`; returns MOE_ERR_INVALID_ARG for a bad format, count
+ * or buffer size. */
+#define MOE_MFMA_PROBE_THREADS 512
+#define MOE_MFMA_PROBE_OPERAND_BYTES (64u * 64u * 16u * 16u)
+int32_t moe_mfma_rate_probe(int32_t format, int32_t blocks, int64_t iters, const void* operands,
+                            size_t operand_bytes, int64_t* stamps, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,10 @@ MOE_Y_BF16 = 1
 # every symbol include/moe_ffn.h declares
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_scratch_bytes", "moe_ffn_plan",
            "moe_workspace_init", "moe_dispatch_layout", "moe_ffn_forward", "moe_combine_check",
-           "moe_store_burst_probe", "moe_predict_schedule", "moe_ffn_forward_noalloc")
+           "moe_store_burst_probe", "moe_predict_schedule", "moe_ffn_forward_noalloc",
+           "moe_mfma_rate_probe")
+MFMA_PROBE_THREADS = 512
+MFMA_PROBE_OPERAND_BYTES = 64 * 64 * 16 * 16
 NOALLOC_WORKSPACE_BYTES = 64 << 20
 NOALLOC_MAX_SCHED_ROWS = 16384
 
@@ -128,6 +131,8 @@ def load(path: str | None = None):
     lib.moe_combine_check.argtypes = [P(MoeShape), P(MoeLayout), P(c_vp), c_vp, c_i32, c_vp, c_vp, c_vp]
     lib.moe_store_burst_probe.restype = c_i32
     lib.moe_store_burst_probe.argtypes = [P(MoeBurstParams), c_vp, ctypes.c_size_t, c_vp, c_vp]
+    lib.moe_mfma_rate_probe.restype = c_i32
+    lib.moe_mfma_rate_probe.argtypes = [c_i32, c_i32, ctypes.c_int64, c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp]
     lib.moe_predict_schedule.restype = c_i32
     lib.moe_predict_schedule.argtypes = [P(MoeShape), P(MoePlan), P(c_i32), P(MoeSchedParams),
                                          P(MoeSchedulePrediction)]
@@ -194,6 +199,12 @@ def combine_check(shape, layout, comb_ptrs, y_ptr, y_dtype, status_ptr, report_p
     check(load().moe_combine_check(ctypes.byref(shape), ctypes.byref(layout),
                                    ptr_array(comb_ptrs), y_ptr, y_dtype, status_ptr, report_ptr, stream),
           "moe_combine_check")
+
+
+def mfma_rate_probe(fmt: int, blocks: int, iters: int, operands_ptr: int, operand_bytes: int, stamps_ptr: int,
+                    sink_ptr: int, stream: int):
+    check(load().moe_mfma_rate_probe(fmt, blocks, iters, operands_ptr, operand_bytes, stamps_ptr, sink_ptr, stream),
+          "moe_mfma_rate_probe")
 
 
 def store_burst_probe(params: MoeBurstParams, dst_ptr: int, dst_bytes: int, stamps_ptr: int,

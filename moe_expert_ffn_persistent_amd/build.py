@@ -21,6 +21,7 @@ LIB = os.path.join(PKG, "libmoe_ffn.so")
 ARCH = "gfx950"
 
 SOURCES = ["layout.hip", "ffn_bf16.hip", "ffn_fp8.hip", "ffn_w4a8.hip", "combine.hip", "burst.hip",
+           "mfma_probe.hip",
            "api.cpp", "planner.cpp"]
 
 COMMON = [

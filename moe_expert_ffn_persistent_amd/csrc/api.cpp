@@ -496,6 +496,20 @@ int32_t moe_combine_check(const moe_shape* s, const moe_layout* lay, void* const
   return launch_check(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int32_t moe_mfma_rate_probe(int32_t format, int32_t blocks, int64_t iters, const void* operands,
+                            size_t operand_bytes, int64_t* stamps, float* sink, void* stream) {
+  static_assert(MOE_MFMA_PROBE_THREADS == 512, "probe workgroup size");
+  if (format < 0 || format > 2 || blocks < 1 || blocks > 65535 || iters < 1 || !operands || !stamps || !sink)
+    return MOE_ERR_INVALID_ARG;
+  if (operand_bytes < mfma_probe_operand_bytes() || mfma_probe_operand_bytes() != MOE_MFMA_PROBE_OPERAND_BYTES ||
+      mfma_probe_threads() != MOE_MFMA_PROBE_THREADS)
+    return MOE_ERR_INVALID_ARG;
+  return launch_mfma_probe(format, blocks, (long long)iters, operands, reinterpret_cast<long long*>(stamps), sink,
+                           (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 int32_t moe_store_burst_probe(const moe_burst_params* prm, void* dst, size_t dst_bytes, uint32_t* stamps,
                               void* stream) {
   if (!prm || !dst || !stamps) return MOE_ERR_INVALID_ARG;

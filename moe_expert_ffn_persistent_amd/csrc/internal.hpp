@@ -48,6 +48,12 @@ struct BurstArgs {
 
 hipError_t launch_burst(const BurstArgs& a, hipStream_t stream);
 
+// MFMA issue-rate probe (mfma_probe.hip)
+size_t mfma_probe_operand_bytes();
+int mfma_probe_threads();
+hipError_t launch_mfma_probe(int format, int blocks, long long iters, const void* ops, long long* stamps,
+                             float* sink, hipStream_t stream);
+
 // Arguments of the persistent FFN kernel. Passed by value; the slice tables
 // are copied to LDS at kernel start.
 struct FfnArgs {
