@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 4
+#define MOE_FFN_ABI_VERSION 5
 #define MOE_MAX_SLICES 64
 #define MOE_MAX_LOCAL_EXPERTS 256
 #define MOE_TRACE_WORDS 10      /* uint32 words per task record */

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     _lib_or_skip()
-    assert _lib.abi_version() == 4
+    assert _lib.abi_version() == 5
     for st in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(st) and "unknown" not in _lib.status_string(st)
     assert "unknown" in _lib.status_string(-99)
