@@ -14,10 +14,13 @@
 //                 softmax over the kept z.
 //   layout_count  one wavefront per chunk of 256 flat pairs: per-expert
 //                 counts of the chunk.
-//   layout_scan   one workgroup: wavefront prefix scans over the chunk
-//                 counts of each expert (chunk bases), then over experts
-//                 (row and scheduler-row offsets) and the totals.
-//   layout_place  one wavefront per chunk: stable placement. Pairs are taken
+//   layout_scan_cols  one workgroup per local expert: the prefix scan of
+//                 its chunk counts (each chunk's first row of the expert)
+//                 and its count.
+//   layout_place  one wavefront per chunk: the offsets over experts (row
+//                 and scheduler-row offsets; the first workgroup also
+//                 stores them and the totals), then stable placement
+//                 (layout_offsets stores them for an empty batch). Pairs are taken
 //                 64 at a time in flat order; lanes with the same expert are
 //                 grouped with ballots and ranked by the popcount of the
 //                 lower lanes, so rows of an expert keep ascending f.
@@ -175,80 +178,104 @@ __global__ void __launch_bounds__(kWave) layout_count(LayoutArgs a) {
   for (int e = lane; e < a.L; e += kWave) a.block_counts[(size_t)blockIdx.x * a.L + e] = s_cnt[e];
 }
 
-// ints of block counts staged in LDS per pass: 128 KiB, so that the counts
-// of up to 992 chunks of 32 experts (253,952 pairs) take one pass
-constexpr int kScanLds = 32768;
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 4;   // consecutive chunks per thread per pass
 
-// Exclusive scan of every expert's column of block_counts over the chunks,
-// then the per-expert totals, row and tile offsets. The counts pass through
-// LDS in row batches (coalesced global traffic; rows padded to L+1 ints so a
-// column read hits distinct banks); one wavefront scans one column at a time.
-__global__ void __launch_bounds__(1024) layout_scan(LayoutArgs a) {
-  extern __shared__ int s_tot[];   // [L] running per-expert totals
-  __shared__ int s_buf[kScanLds];   // staging rows
+// One workgroup per local expert e: the exclusive scan of column e of
+// block_counts over the chunks (each chunk's first row of expert e), in
+// place, and counts[e]. A thread takes kScanPer consecutive chunks (their
+// loads in flight together), the workgroup scans the thread sums: wavefront
+// scans, then one wavefront over the wavefront totals.
+__global__ void __launch_bounds__(kScanThreads) layout_scan_cols(LayoutArgs a) {
+  __shared__ int s_wsum[kScanThreads / kWave];
+  const int e = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  const int L = a.L, LP = a.L + 1;
-  const int rows_per_pass = kScanLds / LP;
-  for (int e = threadIdx.x; e < L; e += blockDim.x) s_tot[e] = 0;
-  for (int c0 = 0; c0 < a.nchunks; c0 += rows_per_pass) {
-    const int nr = min(rows_per_pass, a.nchunks - c0);
+  int carry = 0;
+  for (int c0 = 0; c0 < a.nchunks; c0 += kScanThreads * kScanPer) {
+    const int cb = c0 + threadIdx.x * kScanPer;
+    int v[kScanPer];
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u)
+      v[u] = cb + u < a.nchunks ? a.block_counts[(size_t)(cb + u) * a.L + e] : 0;
+    int tsum = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) tsum += v[u];
+    const int winc = wave_inclusive_scan(tsum);
+    if (lane == kWave - 1) s_wsum[wave] = winc;
     __syncthreads();
-    for (int i = threadIdx.x; i < nr * L; i += blockDim.x)
-      s_buf[(i / L) * LP + i % L] = a.block_counts[(size_t)c0 * L + i];
-    __syncthreads();
-    for (int e = wave; e < L; e += nwaves) {
-      int carry = s_tot[e];
-      for (int r0 = 0; r0 < nr; r0 += kWave) {
-        const int r = r0 + lane;
-        const int v = r < nr ? s_buf[r * LP + e] : 0;
-        const int inc = wave_inclusive_scan(v);
-        if (r < nr) s_buf[r * LP + e] = carry + inc - v;
-        carry += __shfl(inc, kWave - 1, kWave);
-      }
-      if (lane == 0) s_tot[e] = carry;
+    if (wave == 0) {
+      const int w = lane < kScanThreads / kWave ? s_wsum[lane] : 0;
+      const int wi = wave_inclusive_scan(w);
+      if (lane < kScanThreads / kWave) s_wsum[lane] = wi - w;   // exclusive over wavefronts
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nr * L; i += blockDim.x)
-      a.block_counts[(size_t)c0 * L + i] = s_buf[(i / L) * LP + i % L];
+    int run = carry + s_wsum[wave] + winc - tsum;   // exclusive prefix of this thread's first chunk
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      if (cb + u < a.nchunks) a.block_counts[(size_t)(cb + u) * a.L + e] = run;
+      run += v[u];
+    }
+    // the pass total, from the last thread's inclusive sum
+    const int total = __shfl(winc, kWave - 1, kWave);
+    __syncthreads();
+    if (wave == kScanThreads / kWave - 1 && lane == 0) s_wsum[0] = s_wsum[wave] + total;
+    __syncthreads();
+    carry += s_wsum[0];
+    __syncthreads();
   }
-  __syncthreads();
-  // 2) over experts: row offsets, scheduler-row offsets, totals
-  if (wave == 0) {
-    int row_carry = 0, tile_carry = 0, mx = 0, active = 0;
-    for (int e0 = 0; e0 < a.L; e0 += kWave) {
-      const int e = e0 + lane;
-      const int cnt = e < a.L ? s_tot[e] : 0;
-      const int tiles = (cnt + a.block_m - 1) / a.block_m;
-      const int rinc = wave_inclusive_scan(cnt);
-      const int tinc = wave_inclusive_scan(tiles);
-      if (e < a.L) {
-        a.counts[e] = cnt;
+  if (threadIdx.x == 0) a.counts[e] = carry;
+}
+
+// The expert-level offsets from counts[]: one wavefront scans the experts
+// (row offsets, scheduler-row offsets, the largest count, the active
+// experts). Every lane < L ends with its expert's row offset in *rowoff.
+// With `write`, the offsets, the totals and the end entries are stored.
+__device__ __forceinline__ void expert_offsets(const LayoutArgs& a, int* s_rowoff, bool write) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int row_carry = 0, tile_carry = 0, mx = 0, active = 0;
+  for (int e0 = 0; e0 < a.L; e0 += kWave) {
+    const int e = e0 + lane;
+    const int cnt = e < a.L ? a.counts[e] : 0;
+    const int tiles = (cnt + a.block_m - 1) / a.block_m;
+    const int rinc = wave_inclusive_scan(cnt);
+    const int tinc = wave_inclusive_scan(tiles);
+    if (e < a.L) {
+      s_rowoff[e] = row_carry + rinc - cnt;
+      if (write) {
         a.row_offset[e] = row_carry + rinc - cnt;
         a.tile_offset[e] = tile_carry + tinc - tiles;
       }
-      row_carry += __shfl(rinc, kWave - 1, kWave);
-      tile_carry += __shfl(tinc, kWave - 1, kWave);
-      mx = max(mx, wave_max(cnt));
-      active += wave_sum(cnt > 0 ? 1 : 0);
     }
-    if (lane == 0) {
-      a.row_offset[a.L] = row_carry;
-      a.tile_offset[a.L] = tile_carry;
-      a.totals[0] = row_carry;
-      a.totals[1] = tile_carry;
-      a.totals[2] = mx;
-      a.totals[3] = active;
-    }
+    row_carry += __shfl(rinc, kWave - 1, kWave);
+    tile_carry += __shfl(tinc, kWave - 1, kWave);
+    mx = max(mx, wave_max(cnt));
+    active += wave_sum(cnt > 0 ? 1 : 0);
   }
+  if (write && lane == 0) {
+    a.row_offset[a.L] = row_carry;
+    a.tile_offset[a.L] = tile_carry;
+    a.totals[0] = row_carry;
+    a.totals[1] = tile_carry;
+    a.totals[2] = mx;
+    a.totals[3] = active;
+  }
+}
+
+// The offsets alone, for an empty batch (no chunk to place).
+__global__ void __launch_bounds__(kWave) layout_offsets(LayoutArgs a) {
+  extern __shared__ int s_rowoff[];   // [L]
+  expert_offsets(a, s_rowoff, true);
 }
 
 __global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
   extern __shared__ int s_base[];   // [L] next row of each expert in this chunk
   const int lane = threadIdx.x;
-  for (int e = lane; e < a.L; e += kWave)
-    s_base[e] = a.row_offset[e] + a.block_counts[(size_t)blockIdx.x * a.L + e];
+  // every workgroup scans the experts itself (L values); the first one also
+  // stores the offsets and totals
+  expert_offsets(a, s_base, blockIdx.x == 0);
+  __syncthreads();
+  for (int e = lane; e < a.L; e += kWave) s_base[e] += a.block_counts[(size_t)blockIdx.x * a.L + e];
   __syncthreads();
   const int total = a.N * a.k;
   const int f0 = blockIdx.x * kLayoutChunk;
@@ -306,8 +333,9 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   }
   const size_t lds = sizeof(int) * (size_t)a.L;
   if (a.nchunks > 0) layout_count<<<a.nchunks, kWave, lds, stream>>>(a);
-  layout_scan<<<1, 1024, lds, stream>>>(a);
+  layout_scan_cols<<<a.L, kScanThreads, 0, stream>>>(a);
   if (a.nchunks > 0) layout_place<<<a.nchunks, kWave, lds, stream>>>(a);
+  else layout_offsets<<<1, kWave, lds, stream>>>(a);
   return hipGetLastError();
 }
 
