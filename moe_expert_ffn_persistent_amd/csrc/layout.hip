@@ -9,9 +9,11 @@
 // integer work except the router softmax, and it must be bit-exact.
 //
 // Kernels, all launched on the caller's stream, no host round trip:
-//   route_topk    one wavefront per token: k rounds of a wavefront argmax
-//                 over (z desc, index asc) by DPP reductions of order keys,
-//                 softmax over the kept z.
+//   route_topk16  (E <= 128, or E <= 256 with N >= 16384) one 16-lane row per token, four tokens per
+//                 wavefront: k rounds of a row argmax over (z desc, index
+//                 asc) by DPP row reductions of order keys, softmax over the
+//                 kept z.
+//   route_topk    (otherwise) the same with one wavefront per token.
 //   layout_count  one wavefront per chunk of 256 flat pairs: per-expert
 //                 counts of the chunk.
 //   layout_scan_cols  one workgroup per local expert: the prefix scan of
@@ -159,6 +161,89 @@ __global__ void __launch_bounds__(256) route_topk(LayoutArgs a) {
   if (lane < a.k) {
     a.topk_idx[(size_t)n * a.k + lane] = myi;
     a.topk_w[(size_t)n * a.k + lane] = ex / sum;
+  }
+}
+
+// Maximum (kMin false) or minimum of v over each 16-lane row of the
+// wavefront, returned to every lane of the row: four row shifts leave the
+// result in lane 15 of the row (lanes whose shifted source lies outside the
+// row keep the identity), which is then read by the whole row.
+template <bool kMin>
+__device__ __forceinline__ int row_extreme(int v) {
+  constexpr int id = kMin ? INT_MAX : INT_MIN;
+  auto f = [](int a, int b) { return kMin ? min(a, b) : max(a, b); };
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+  v = f(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+  const int lane = threadIdx.x & (kWave - 1);
+  return __shfl(v, (lane & ~15) | 15, kWave);
+}
+
+// As route_topk with one token per 16-lane row (four per wavefront), for
+// E <= 16 * PER; PER = 4, 8, 16. Lane l of a row holds experts l, l+16, ...
+// Each of the k rounds takes every lane's best remaining expert (largest
+// key, then lowest index, which within a lane is the lowest slot), the row's
+// largest key, and among the lanes holding it the lowest expert index; the
+// winning lane retires that expert.
+template <int PER>
+__global__ void __launch_bounds__(256) route_topk16(LayoutArgs a) {
+  constexpr int kRow = 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rl = lane & (kRow - 1), rbase = lane & ~(kRow - 1);
+  const int n = blockIdx.x * (blockDim.x / kRow) + threadIdx.x / kRow;
+  if (n >= a.N) return;   // whole rows: the row count per wavefront is fixed
+  float z[PER];
+  int key[PER];
+  const float* row = a.logits + (size_t)n * a.E;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = rl + i * kRow;
+    float v = -INFINITY;
+    if (e < a.E) {
+      v = row[e];
+      if (a.bias) v = v + a.bias[e];
+    }
+    z[i] = v;
+    key[i] = e < a.E ? order_key(v) : INT_MIN;   // below NaN: never taken while k <= E
+  }
+  float myz = 0.f;   // lane j < k of the row keeps the j-th selection
+  int myi = 0;
+  for (int j = 0; j < a.k; ++j) {
+    int hk = key[0], hs = 0;
+#pragma unroll
+    for (int i = 1; i < PER; ++i)
+      if (key[i] > hk) {
+        hk = key[i];
+        hs = i;
+      }
+    const int best = row_extreme<false>(hk);
+    const int e = row_extreme<true>(hk == best ? rl + kRow * hs : INT_MAX);
+    const int wl = e & (kRow - 1), ws = e / kRow;
+    float zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i == ws) zs = z[i];
+    const float wz = __int_as_float(__shfl(__float_as_int(zs), rbase | wl, kWave));
+    if (rl == wl) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == ws) key[i] = INT_MIN;
+    }
+    if (rl == j) {
+      myz = wz;
+      myi = e;
+    }
+  }
+  // softmax over the kept values; the first selection is the largest
+  const float zmax = __shfl(myz, rbase, kWave);
+  const float ex = rl < a.k ? expf(myz - zmax) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int d = kRow / 2; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, kWave);
+  if (rl < a.k) {
+    a.topk_idx[(size_t)n * a.k + rl] = myi;
+    a.topk_w[(size_t)n * a.k + rl] = ex / sum;
   }
 }
 
@@ -323,13 +408,23 @@ __global__ void __launch_bounds__(kWave) layout_place(LayoutArgs a) {
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (a.logits && a.N > 0) {
-    const int per_block = 4;   // tokens (wavefronts) per workgroup
-    const dim3 grid((a.N + per_block - 1) / per_block), block(per_block * kWave);
-    if (a.E <= 64) route_topk<1><<<grid, block, 0, stream>>>(a);
-    else if (a.E <= 128) route_topk<2><<<grid, block, 0, stream>>>(a);
-    else if (a.E <= 256) route_topk<4><<<grid, block, 0, stream>>>(a);
-    else if (a.E <= 512) route_topk<8><<<grid, block, 0, stream>>>(a);
-    else route_topk<16><<<grid, block, 0, stream>>>(a);
+    // four tokens per wavefront where it measured faster on MI355X: E <= 128
+    // (20% at 8 x 8192 tokens, 128 experts), and E <= 256 with many tokens
+    // (8% at 8 x 4096 tokens; 8% slower at 8 x 512, where fewer wavefronts
+    // leave the routing latency-bound)
+    if (a.E <= 128 || (a.E <= 256 && a.N >= 16384)) {
+      const int per_block = 16;   // tokens (16-lane rows) per workgroup
+      const dim3 grid((a.N + per_block - 1) / per_block), block(256);
+      if (a.E <= 64) route_topk16<4><<<grid, block, 0, stream>>>(a);
+      else if (a.E <= 128) route_topk16<8><<<grid, block, 0, stream>>>(a);
+      else route_topk16<16><<<grid, block, 0, stream>>>(a);
+    } else {
+      const int per_block = 4;   // tokens (wavefronts) per workgroup
+      const dim3 grid((a.N + per_block - 1) / per_block), block(per_block * kWave);
+      if (a.E <= 256) route_topk<4><<<grid, block, 0, stream>>>(a);
+      else if (a.E <= 512) route_topk<8><<<grid, block, 0, stream>>>(a);
+      else route_topk<16><<<grid, block, 0, stream>>>(a);
+    }
   }
   const size_t lds = sizeof(int) * (size_t)a.L;
   if (a.nchunks > 0) layout_count<<<a.nchunks, kWave, lds, stream>>>(a);

@@ -80,28 +80,59 @@ def test_layout_from_given_topk_and_ties():
     _check_layout(wl, lb, idx2, w2, ffn.plan.block_m, routed=False)
 
 
-def test_routing_ties_across_lanes_and_slots():
-    # 256 experts: lane l of the routing wavefront holds experts l, l+64, l+128
-    # and l+192, so equal logits can tie within a lane (different slots) and
-    # across lanes; -0 and +0 must tie; NaN sorts after every number and
-    # -inf after every finite value (a stable sort of -z)
-    wl = mi.Workload("ties256", 2, 32, 256, 8, 0, 32, 256, 128, "bf16", False, 7)
+@pytest.mark.parametrize("E", [256, 128])
+def test_routing_ties_across_lanes_and_slots(E):
+    # E = 256 (64 tokens: one wavefront per token, lane l holds experts l,
+    # l+64, ...) and E = 128 (four tokens per wavefront, lane l of a token's
+    # 16-lane row holds experts l, l+16, ...): equal logits tie within a lane
+    # (different slots) and across lanes; -0 and +0 must tie; NaN sorts after
+    # every number and -inf after every finite value (a stable sort of -z)
+    wl = mi.Workload(f"ties{E}", 2, 32, E, 8, 0, 32, 256, 128, "bf16", False, 7)
     rng = np.random.default_rng(11)
-    logits = rng.standard_normal((64, 256)).astype(np.float32)
+    logits = rng.standard_normal((64, E)).astype(np.float32)
     logits[:16] = 0.0
-    logits[:16][rng.random((16, 256)) < 0.5] = -0.0          # mixed-sign zeros: experts 0..7 win
+    logits[:16][rng.random((16, E)) < 0.5] = -0.0            # mixed-sign zeros: experts 0..7 win
+    q = E // 4
+    tie_cols = [0, 8, q, q + 8, 2 * q, 2 * q + 8, 3 * q, 3 * q + 8]
     logits[16:32] = -np.abs(logits[16:32]) - 1.0
-    logits[16:32][:, [200, 136, 72, 8, 64, 128, 192, 0]] = 1.0
+    logits[16:32][:, tie_cols[::-1]] = 1.0
     for r in range(32, 48):
-        cols = rng.choice(256, 12, replace=False)
+        cols = rng.choice(E, 12, replace=False)
         logits[r, cols[:6]] = np.nan
         logits[r, cols[6:]] = -np.inf
-    logits[48:56, :250] = -np.inf                             # the finite six, then -inf by index
+    logits[48:56, :E - 6] = -np.inf                           # the finite six, then -inf by index
+    logits[56:64] = -np.abs(logits[56:64]) - 1.0
+    logits[56:64][:, [49, 33, 17, 1, 48, 32, 16, 0]] = 2.0     # two lanes, four slots each
     idx_ref, w_ref = mo.route(logits, None, 8)
     assert (idx_ref[:16] == np.arange(8)).all()
-    assert (idx_ref[16:32] == [0, 8, 64, 72, 128, 136, 192, 200]).all()
-    assert (np.sort(idx_ref[48:56, :6], axis=1) == np.arange(250, 256)).all()
+    assert (idx_ref[16:32] == tie_cols).all()
+    assert (np.sort(idx_ref[48:56, :6], axis=1) == np.arange(E - 6, E)).all()
     assert (idx_ref[48:56, 6:] == [0, 1]).all()
+    assert (idx_ref[56:64] == [0, 1, 16, 17, 32, 33, 48, 49]).all()
+    ffn = make_ffn(wl)
+    lb = ffn.layout(logits=to_dev(logits))
+    torch.cuda.synchronize()
+    _check_layout(wl, lb, idx_ref, w_ref, ffn.plan.block_m)
+
+
+def test_routing_sixteen_lane_rows_at_256_experts():
+    # E = 256 with N >= 16384 takes the four-tokens-per-wavefront kernel:
+    # ties, signed zeros, NaN and -inf in a batch large enough for it
+    E = 256
+    wl = mi.Workload("rows256", 8, 2048, E, 8, 0, 32, 256, 128, "bf16", False, 8)
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((wl.num_tokens, E)).astype(np.float32)
+    logits[:1000] = 0.0
+    logits[:1000][rng.random((1000, E)) < 0.5] = -0.0
+    logits[1000:2000] = -np.abs(logits[1000:2000]) - 1.0
+    logits[1000:2000][:, [49, 33, 17, 1, 48, 32, 16, 0]] = 2.0
+    for r in range(2000, 3000):
+        cols = rng.choice(E, 12, replace=False)
+        logits[r, cols[:6]] = np.nan
+        logits[r, cols[6:]] = -np.inf
+    idx_ref, w_ref = mo.route(logits, None, 8)
+    assert (idx_ref[:1000] == np.arange(8)).all()
+    assert (idx_ref[1000:2000] == [0, 1, 16, 17, 32, 33, 48, 49]).all()
     ffn = make_ffn(wl)
     lb = ffn.layout(logits=to_dev(logits))
     torch.cuda.synchronize()
